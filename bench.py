@@ -1,0 +1,399 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid GQA attention layer's hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+RoPE on the new keys, the KV-cache append, prefill attention (Q-RoPE fused in its
+prologue, sigmoid gate in its epilogue), then the single-token decode (RoPE, append,
+split-KV partials and their log-sum-exp combine).
+
+Default workload (the 1M-context full layer, B=1): a cache holding positions
+0..1044479, a chunked prefill of 4096 queries at positions 1044480..1048575, then one
+decode at position 1048576 over 1048577 keys.  Other workloads (--workload 2|3|4) are
+the 32K sliding prefill, the 128K full prefill and the B=32 mixed decode at 128K.
+
+Prints one JSON line.  `value` is the prefill attention throughput of the whole step
+(algorithmic prefill FLOP / step time); the decode KV bandwidth and per-kernel rates,
+measured with HIP events on the library's stream, are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "prefill attn TFLOP/s (%MFMA peak); decode KV GB/s (%HBM) at 128K/1M"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+HQ, HKV, D, WINDOW = 16, 4, 256, 512
+KV_BYTES_PER_TOKEN = 2 * HKV * D * 2   # K and V rows of one token, one layer
+FLOP_PER_PAIR = 4 * D                  # QK^T and PV per visible (query, key, head)
+
+
+def prefill_pairs(sq: int, pos0: int, kind: str) -> int:
+    """Visible (query, key) pairs of one head for queries at pos0 .. pos0+sq-1."""
+    if kind == "full":
+        return sq * pos0 + sq * (sq + 1) // 2
+    n_short = max(0, min(sq, WINDOW - pos0))
+    return n_short * pos0 + n_short * (n_short + 1) // 2 + (sq - n_short) * WINDOW
+
+
+class Timer:
+    """HIP events around each launch of one stage, on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+class Stages:
+    def __init__(self, names):
+        self.t = {n: [] for n in names}
+
+    def time(self, name):
+        s = Timer()
+        self.t[name].append(s)
+        return s
+
+    def mean_ms(self, name):
+        xs = self.t[name]
+        return sum(x.mean_ms() for x in xs) / max(1, len(xs))
+
+    def clear(self):
+        for k in self.t:
+            self.t[k] = []
+
+
+# ------------------------------------------------------------------------ workloads --
+def _cap(n: int) -> int:
+    return synth.round_up(n, 64)
+
+
+class PrefillWorkload:
+    """Workloads 2 and 3: one layer's prefill from position 0; K/V consumed in place."""
+
+    def __init__(self, idx: int, device="cuda"):
+        from full_gqa_attention_hattn_amd import hattn
+        self.h = hattn
+        W = synth.WORKLOADS[idx]
+        self.W, self.kind = W, W.params["kind"]
+        B, S = W.params["B"], W.params["S"]
+        self.B, self.S = B, S
+        self.cfg = hattn.preset(self.kind)
+        inp = synth.layer_inputs(W.seed, B, S, device)
+        self.q, self.k_src, self.v, self.gate = inp["q"], inp["k"], inp["v"], inp["gate"]
+        self.k = torch.empty_like(self.k_src)
+        self.pos0 = synth.positions(0, B, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(B, S, HQ, dtype=torch.float32, device=device)
+        self.stages = Stages(["rope_k", "prefill"])
+        self.prefill_flop = B * HQ * FLOP_PER_PAIR * prefill_pairs(S, 0, self.kind)
+        self.decode_bytes = 0
+
+    def step(self):
+        h = self.h
+        self.k.copy_(self.k_src)
+        with self.stages.time("rope_k"):
+            h.rope_qk(self.cfg, None, self.k, self.pos0)
+        with self.stages.time("prefill"):
+            h.prefill(self.cfg, self.q, self.k, self.v, self.pos0, self.gate, self.out, self.lse,
+                      rope_q_fused=True)
+
+
+class MixedDecodeWorkload:
+    """Workload 4: B=32 new tokens at position 131072; one full layer reading a 131072-token
+    cache and three sliding layers reading full 512-slot rings."""
+
+    def __init__(self, device="cuda"):
+        from full_gqa_attention_hattn_amd import hattn
+        self.h = hattn
+        W = synth.WORKLOADS[4]
+        self.W = W
+        B, p = W.params["B"], W.params["pos"]
+        self.B, self.p = B, p
+        self.cap = _cap(p + 1)
+        self.layers = []
+        for li, kind in enumerate(["full", "sliding", "sliding", "sliding"]):
+            cfg = hattn.preset(kind)
+            cap = self.cap if kind == "full" else WINDOW
+            n_filled = p if kind == "full" else WINDOW
+            cache = synth.cache_inputs(W.seed, B, cap, n_filled, device, layer=li)
+            new = synth.layer_inputs(W.seed, B, 1, device, layer=li)
+            L = dict(kind=kind, cfg=cfg, cap=cap, K=cache["cache_k"], V=cache["cache_v"],
+                     q=new["q"], k_src=new["k"], v=new["v"], gate=new["gate"],
+                     k=torch.empty_like(new["k"]),
+                     out=torch.empty_like(new["q"]),
+                     lse=torch.empty(B, 1, HQ, dtype=torch.float32, device=device),
+                     ws=hattn.alloc_workspace(cfg, B, cap, device),
+                     slots=torch.empty(B, 1, dtype=torch.int32, device=device))
+            self.layers.append(L)
+        self.pos = synth.positions(p, B, device)
+        self.stages = Stages(["rope_k", "append", "decode_full", "decode_sliding"])
+        self.prefill_flop = 0
+        n_full = min(p + 1, self.cap)
+        self.decode_bytes = B * KV_BYTES_PER_TOKEN * (n_full + 3 * min(p + 1, WINDOW))
+        self.decode_bytes_full = B * KV_BYTES_PER_TOKEN * n_full
+
+    def step(self):
+        h = self.h
+        for L in self.layers:
+            L["k"].copy_(L["k_src"])
+            with self.stages.time("rope_k"):
+                h.rope_qk(L["cfg"], None, L["k"], self.pos)
+            with self.stages.time("append"):
+                h.kv_append(L["cfg"], L["k"], L["v"], L["K"], L["V"], self.pos, L["slots"])
+            with self.stages.time("decode_full" if L["kind"] == "full" else "decode_sliding"):
+                h.decode(L["cfg"], L["q"], L["K"], L["V"], self.pos, L["gate"], L["out"],
+                         L["lse"], L["ws"], rope_q_fused=True)
+
+
+class Full1MWorkload:
+    """Workload 5: 1M-context full layer, B=1 -- chunked prefill then one decode."""
+
+    def __init__(self, device="cuda"):
+        from full_gqa_attention_hattn_amd import hattn
+        self.h = hattn
+        W = synth.WORKLOADS[5]
+        self.W = W
+        self.L0, self.C, self.pd = W.params["cache_len"], W.params["chunk"], W.params["decode_pos"]
+        self.cap = _cap(self.pd + 1)
+        self.cfg = hattn.preset("full")
+        cache = synth.cache_inputs(W.seed, 1, self.cap, self.L0, device, layer=0)
+        self.K, self.V = cache["cache_k"], cache["cache_v"]
+        ch = synth.layer_inputs(W.seed, 1, self.C, device, layer=1)
+        self.q, self.k_src, self.v, self.gate = ch["q"], ch["k"], ch["v"], ch["gate"]
+        self.k = torch.empty_like(self.k_src)
+        dc = synth.layer_inputs(W.seed, 1, 1, device, layer=2)
+        self.qd, self.kd_src, self.vd, self.gd = dc["q"], dc["k"], dc["v"], dc["gate"]
+        self.kd = torch.empty_like(self.kd_src)
+        self.pos0 = synth.positions(self.L0, 1, device)
+        self.posd = synth.positions(self.pd, 1, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(1, self.C, HQ, dtype=torch.float32, device=device)
+        self.outd = torch.empty_like(self.qd)
+        self.lsed = torch.empty(1, 1, HQ, dtype=torch.float32, device=device)
+        self.ws = hattn.alloc_workspace(self.cfg, 1, self.cap, device)
+        self.slots = torch.empty(1, self.C, dtype=torch.int32, device=device)
+        self.slotsd = torch.empty(1, 1, dtype=torch.int32, device=device)
+        self.stages = Stages(["rope_k", "append", "prefill", "decode"])
+        self.prefill_flop = HQ * FLOP_PER_PAIR * prefill_pairs(self.C, self.L0, "full")
+        self.decode_bytes = KV_BYTES_PER_TOKEN * (self.pd + 1)
+
+    def step(self):
+        h = self.h
+        self.k.copy_(self.k_src)
+        with self.stages.time("rope_k"):
+            h.rope_qk(self.cfg, None, self.k, self.pos0)
+        with self.stages.time("append"):
+            h.kv_append(self.cfg, self.k, self.v, self.K, self.V, self.pos0, self.slots)
+        with self.stages.time("prefill"):
+            h.prefill(self.cfg, self.q, self.K, self.V, self.pos0, self.gate, self.out, self.lse,
+                      rope_q_fused=True)
+        self.kd.copy_(self.kd_src)
+        with self.stages.time("rope_k"):
+            h.rope_qk(self.cfg, None, self.kd, self.posd)
+        with self.stages.time("append"):
+            h.kv_append(self.cfg, self.kd, self.vd, self.K, self.V, self.posd, self.slotsd)
+        with self.stages.time("decode"):
+            h.decode(self.cfg, self.qd, self.K, self.V, self.posd, self.gd, self.outd, self.lsed,
+                     self.ws, rope_q_fused=True)
+
+
+def make_workload(idx: int, device="cuda"):
+    if idx in (2, 3):
+        return PrefillWorkload(idx, device)
+    if idx == 4:
+        return MixedDecodeWorkload(device)
+    if idx == 5:
+        return Full1MWorkload(device)
+    raise ValueError(f"no bench workload {idx} (1 is the parity-only tiny case)")
+
+
+# ---------------------------------------------------------------------- cpu baseline --
+def cpu_baseline(wl, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload, timed on the
+    host's cores.  Reported in the metric's unit (TFLOP/s of attention work; GB/s of KV
+    for the decode-only workload)."""
+    import oracle as O
+    torch.set_num_threads(os.cpu_count() or 1)
+    cores = torch.get_num_threads()
+    if isinstance(wl, Full1MWorkload):
+        rows = [wl.C - 1 - i for i in range(4)]
+        kc = wl.K[0, :wl.L0].cpu()
+        vc = wl.V[0, :wl.L0].cpu()
+        k_chunk = wl.k_src[0].cpu()
+        _, kr = O.rope_qk(None, k_chunk, wl.L0, "full")
+        kc = torch.cat([kc.to(torch.float32), kr])
+        vc = torch.cat([vc.to(torch.float32), wl.v[0].cpu().to(torch.float32)])
+        q, g = wl.q[0].cpu(), wl.gate[0].cpu()
+        t0 = time.perf_counter()
+        done = []
+        for r in rows:
+            O.prefill(q, kc, vc, g, wl.L0, "full", rows=torch.tensor([r]))
+            done.append(r)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        flop = sum(HQ * FLOP_PER_PAIR * (wl.L0 + r + 1) for r in done)
+        return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"prefill rows {done} of the 4096-query chunk over the full "
+                          f"{wl.L0 + wl.C}-token cache, all 16 heads ({dt:.1f} s)"}
+    if isinstance(wl, PrefillWorkload):
+        b = 0
+        S = wl.S
+        rows = list(range(S - 1, S - 65, -1))
+        q, g = wl.q[b].cpu(), wl.gate[b].cpu()
+        k_cpu, v = wl.k_src[b].cpu(), wl.v[b].cpu()
+        _, kr = O.rope_qk(None, k_cpu, 0, wl.kind)
+        t0 = time.perf_counter()
+        done = []
+        for r in rows:
+            O.prefill(q, kr, v, g, 0, wl.kind, rows=torch.tensor([r]))
+            done.append(r)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        pairs = sum((r + 1) if wl.kind == "full" else min(r + 1, WINDOW) for r in done)
+        return {"value": HQ * FLOP_PER_PAIR * pairs / dt / 1e12, "unit": "TFLOP/s",
+                "cores": cores, "kind": "oracle",
+                "sample": f"{len(done)} prefill rows of sequence 0 ({dt:.1f} s)"}
+    # mixed decode: full-layer decode of a few sequences
+    L = wl.layers[0]
+    t0 = time.perf_counter()
+    nbytes = 0
+    done = 0
+    for b in range(wl.B):
+        kc = L["K"][b, :wl.p].cpu()
+        vc = L["V"][b, :wl.p].cpu()
+        _, kn = O.rope_qk(None, L["k_src"][b], wl.p, "full")
+        kc = torch.cat([kc.to(torch.float32), kn.cpu()])
+        vc = torch.cat([vc.to(torch.float32), L["v"][b].cpu().to(torch.float32)])
+        O.decode(L["q"][b, 0].cpu(), kc, vc, L["gate"][b, 0].cpu(), wl.p, "full")
+        nbytes += KV_BYTES_PER_TOKEN * (wl.p + 1)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"full-layer decode of {done} of {wl.B} sequences ({dt:.1f} s)"}
+
+
+# --------------------------------------------------------------------------- traffic --
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_src: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "full_gqa_attention_hattn_amd", "csrc", kernel_src)
+    if rec.get("source_sha256") != _sha(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------ main --
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    wl = make_workload(args.workload)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    wl.stages.clear()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    st = wl.stages
+    rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16; no weights needed)"}
+    stage_ms = {k: st.mean_ms(k) for k in st.t if st.t[k]}
+    rec["stage_ms"] = stage_ms
+    if wl.prefill_flop:
+        pf_ms = stage_ms["prefill"]
+        rec["value"] = wl.prefill_flop / (ms * 1e-3) / 1e12
+        rec["unit"] = "TFLOP/s"
+        achieved = wl.prefill_flop / (pf_ms * 1e-3) / 1e12
+        rec["prefill_TFLOPs_kernel"] = achieved
+        rec["prefill_frac_mfma_peak"] = achieved / PEAK_BF16_TFLOPS
+        tr_name = {5: "prefill_full_1m_chunk4096", 3: "prefill_full_b1_s131072",
+                   2: "prefill_sliding_b4_s32768"}[args.workload]
+        rec["roofline"] = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic("prefill.hip", tr_name)}
+    if wl.decode_bytes:
+        dec_ms = sum(stage_ms.get(k, 0.0) for k in ("decode", "decode_full", "decode_sliding"))
+        if isinstance(wl, MixedDecodeWorkload):
+            dec_ms = stage_ms["decode_full"] + 3 * stage_ms["decode_sliding"]
+        gbps = wl.decode_bytes / (dec_ms * 1e-3) / 1e9
+        rec["decode_GBps"] = gbps
+        rec["decode_frac_hbm_peak"] = gbps / PEAK_HBM_GBPS
+        if not wl.prefill_flop:
+            rec["value"] = wl.decode_bytes / (ms * 1e-3) / 1e9
+            rec["unit"] = "GB/s"
+            full_ms = stage_ms["decode_full"]
+            ach = wl.decode_bytes_full / (full_ms * 1e-3) / 1e9
+            rec["roofline"] = {"bound": "hbm", "kernel": "decode_split_kernel+combine",
+                               "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                               "frac": ach / PEAK_HBM_GBPS,
+                               "traffic": measured_traffic("decode.hip", "decode_full_b32_p131072")}
+    W = wl.W
+    rec["config"] = {"workload": W.name, "desc": W.desc, **W.params}
+    if args.cpu_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+// C ABI of libhattn: argument validation, RoPE frequency tables and kernel dispatch.
+// Every check runs on the host before anything is enqueued; kernels add their own range
+// guards for the device-resident position arrays.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/hattn.h"
+#include "hattn_device.h"
+#include "hattn_launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int32_t kWindow = 512;
+constexpr float kLog2e = 1.44269504088896340736f;
+// Largest number of work-items a one-dimensional launch may address.
+constexpr long long kMaxWorkItems = 0xffffffffLL;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+hattn_layer_cfg preset(int32_t kind) {
+  hattn_layer_cfg c{};
+  c.kind = kind;
+  c.n_q_heads = hattn::kHq;
+  c.n_kv_heads = hattn::kHkv;
+  c.head_dim = hattn::kD;
+  c.softmax_scale = 1.0f / 16.0f;
+  c.reserved = 0;
+  if (kind == HATTN_SLIDING) {
+    // [T3] "Sliding window 512": window 512, theta 1e4, all 256 dims rotate.
+    c.window = kWindow;
+    c.rot_dim = 256;
+    c.rope_theta = 1.0e4;
+  } else {
+    // [T3] "Global attention + 5M-base RoPE": theta 5e6, first 64 of 256 dims rotate.
+    c.window = 0;
+    c.rot_dim = 64;
+    c.rope_theta = 5.0e6;
+  }
+  return c;
+}
+
+hattn_status check_cfg(const hattn_layer_cfg* cfg) {
+  if (cfg == nullptr) return HATTN_ERR_NULL;
+  if (cfg->kind != HATTN_SLIDING && cfg->kind != HATTN_FULL) return HATTN_ERR_UNSUPPORTED;
+  const hattn_layer_cfg p = preset(cfg->kind);
+  if (cfg->n_q_heads != p.n_q_heads || cfg->n_kv_heads != p.n_kv_heads ||
+      cfg->head_dim != p.head_dim || cfg->window != p.window || cfg->rot_dim != p.rot_dim ||
+      cfg->rope_theta != p.rope_theta || cfg->softmax_scale != p.softmax_scale ||
+      cfg->reserved != 0)
+    return HATTN_ERR_UNSUPPORTED;
+  return HATTN_OK;
+}
+
+hattn::RopeTable rope_table(const hattn_layer_cfg* cfg) {
+  hattn::RopeTable t{};
+  t.rot_dim = cfg->rot_dim;
+  for (int i = 0; i < cfg->rot_dim / 2; ++i)
+    t.inv_freq[i] = (float)std::pow(cfg->rope_theta, -2.0 * i / (double)cfg->rot_dim);
+  return t;
+}
+
+float scale_log2e(const hattn_layer_cfg* cfg) { return cfg->softmax_scale * kLog2e; }
+
+hattn_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return HATTN_OK;
+  g_last_hip_error = (int32_t)e;
+  return HATTN_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int decode_max_keys(const hattn_layer_cfg* cfg, int32_t cap) {
+  return cfg->kind == HATTN_SLIDING ? cfg->window : cap;
+}
+
+}  // namespace
+
+extern "C" {
+
+hattn_status hattn_cfg_preset(int32_t kind, hattn_layer_cfg* out) {
+  if (out == nullptr) return HATTN_ERR_NULL;
+  if (kind != HATTN_SLIDING && kind != HATTN_FULL) return HATTN_ERR_UNSUPPORTED;
+  *out = preset(kind);
+  return HATTN_OK;
+}
+
+hattn_status hattn_rope_qk(const hattn_layer_cfg* cfg, void* q, void* k, const int32_t* pos0,
+                           int32_t B, int32_t S, void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (B < 0 || S < 0) return HATTN_ERR_SHAPE;
+  const long long ntok = (long long)B * S;
+  if (ntok == 0) return HATTN_OK;
+  if ((q == nullptr && k == nullptr) || pos0 == nullptr) return HATTN_ERR_NULL;
+  if ((q && !aligned16(q)) || (k && !aligned16(k)) || !aligned4(pos0)) return HATTN_ERR_ALIGN;
+  if (ntok * hattn::kHq * hattn::kD >= (1LL << 62) || (ntok + 3) / 4 * 256 > kMaxWorkItems)
+    return HATTN_ERR_SHAPE;
+  const hattn::RopeTable tab = rope_table(cfg);
+  return hip_status(hattn::launch_rope_qk(static_cast<hattn::bf16_t*>(q),
+                                          static_cast<hattn::bf16_t*>(k), pos0, B, S, tab,
+                                          as_stream(stream)));
+}
+
+hattn_status hattn_kv_append(const hattn_layer_cfg* cfg, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, int32_t cap, const int32_t* pos0,
+                             int32_t B, int32_t n, int32_t* slots_out, void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (B < 0 || n < 0 || cap < 1) return HATTN_ERR_SHAPE;
+  if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return HATTN_ERR_RANGE;
+  const long long ntok = (long long)B * n;
+  if (ntok == 0) return HATTN_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !pos0) return HATTN_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(pos0) || (slots_out && !aligned4(slots_out)))
+    return HATTN_ERR_ALIGN;
+  if (ntok * 256 > kMaxWorkItems) return HATTN_ERR_SHAPE;
+  return hip_status(hattn::launch_kv_append(
+      static_cast<const hattn::bf16_t*>(k_new), static_cast<const hattn::bf16_t*>(v_new),
+      static_cast<hattn::bf16_t*>(k_cache), static_cast<hattn::bf16_t*>(v_cache), cap, pos0, B, n,
+      cfg->kind == HATTN_SLIDING ? cfg->window : 0, slots_out, as_stream(stream)));
+}
+
+hattn_status hattn_prefill(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                           const void* v_cache, int32_t cap, const int32_t* pos0, int32_t B,
+                           int32_t Sq, const void* gate, void* out, float* lse, uint32_t flags,
+                           void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (B < 0 || Sq < 0 || cap < 1) return HATTN_ERR_SHAPE;
+  if ((flags & ~(uint32_t)HATTN_ROPE_Q_FUSED) != 0) return HATTN_ERR_UNSUPPORTED;
+  if ((long long)B * Sq == 0) return HATTN_OK;
+  if (!q || !k_cache || !v_cache || !pos0 || !gate || !out) return HATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned2(gate) || !aligned4(pos0) || (lse && !aligned4(lse)))
+    return HATTN_ERR_ALIGN;
+  const long long nqb = ((long long)Sq + 31) / 32;
+  const long long groups = (long long)B * hattn::kHkv * nqb + 8;
+  if (groups * 256 > kMaxWorkItems || (long long)B * Sq >= (1LL << 31) ||
+      (long long)B * cap >= (1LL << 40))
+    return HATTN_ERR_SHAPE;
+  const hattn::RopeTable tab = rope_table(cfg);
+  return hip_status(hattn::launch_prefill(
+      static_cast<const hattn::bf16_t*>(q), static_cast<const hattn::bf16_t*>(k_cache),
+      static_cast<const hattn::bf16_t*>(v_cache), cap, pos0, B, Sq,
+      static_cast<const hattn::bf16_t*>(gate), static_cast<hattn::bf16_t*>(out), lse,
+      cfg->kind == HATTN_SLIDING ? cfg->window : 0, (flags & HATTN_ROPE_Q_FUSED) != 0, tab,
+      scale_log2e(cfg), as_stream(stream)));
+}
+
+size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
+  if (check_cfg(cfg) != HATTN_OK || B < 0 || cap < 1) return 0;
+  if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return 0;
+  if (B == 0) return 0;
+  return hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));
+}
+
+hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                          const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
+                          const void* gate, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (B < 0 || cap < 1) return HATTN_ERR_SHAPE;
+  if ((flags & ~(uint32_t)HATTN_ROPE_Q_FUSED) != 0) return HATTN_ERR_UNSUPPORTED;
+  if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return HATTN_ERR_RANGE;
+  if (B == 0) return HATTN_OK;
+  if (!q || !k_cache || !v_cache || !pos || !gate || !out) return HATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned2(out) ||
+      !aligned2(gate) || !aligned4(pos) || (lse && !aligned4(lse)))
+    return HATTN_ERR_ALIGN;
+  if (B > 65535 || (long long)B * cap >= (1LL << 40)) return HATTN_ERR_SHAPE;
+  const hattn::DecodePlan plan = hattn::decode_plan(B, decode_max_keys(cfg, cap));
+  const size_t need = hattn::decode_workspace_bytes(B, plan);
+  if (workspace == nullptr || workspace_bytes < need) return HATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
+  const hattn::RopeTable tab = rope_table(cfg);
+  return hip_status(hattn::launch_decode(
+      static_cast<const hattn::bf16_t*>(q), static_cast<const hattn::bf16_t*>(k_cache),
+      static_cast<const hattn::bf16_t*>(v_cache), cap, pos, B,
+      static_cast<const hattn::bf16_t*>(gate), static_cast<hattn::bf16_t*>(out), lse,
+      cfg->kind == HATTN_SLIDING ? cfg->window : 0, (flags & HATTN_ROPE_Q_FUSED) != 0, tab,
+      scale_log2e(cfg), plan, workspace, as_stream(stream)));
+}
+
+const char* hattn_status_string(hattn_status status) {
+  switch (status) {
+    case HATTN_OK: return "ok";
+    case HATTN_ERR_NULL: return "a required pointer is NULL";
+    case HATTN_ERR_SHAPE: return "invalid or too large size";
+    case HATTN_ERR_UNSUPPORTED: return "unsupported layer configuration or flag";
+    case HATTN_ERR_RANGE: return "cache capacity or window rule broken";
+    case HATTN_ERR_ALIGN: return "tensor pointer not aligned";
+    case HATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case HATTN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t hattn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

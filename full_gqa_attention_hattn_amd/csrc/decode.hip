@@ -1,0 +1,278 @@
+// Single-token decode for one hybrid-attention layer on CDNA4 (gfx950): split-KV partials
+// followed by a log-sum-exp combine.
+//
+// Full layers read keys 0..pos of a position-indexed cache; sliding layers read the
+// 512-slot ring (slot = position mod 512), every valid slot being inside the window.
+// [T2] "The real bottleneck of a million-token context" (full layers keep the whole
+// history, sliding layers only the last 512 tokens); [T1] "GQA, fused projection and
+// output gating" (4 query heads per KV head; sigmoid head gate).
+//
+// Phase 1 (decode_split_kernel): grid (chunks, B); wave w of a workgroup handles KV head w
+// over the chunk's keys, so a workgroup streams whole 2 KiB cache rows (4 heads x 512 B).
+// Per 32-key step a wave computes S^T = K . Q^T for its 4 query heads on
+// v_mfma_f32_16x16x32_bf16 (K rows feed the MFMA straight from global memory; columns
+// 4..15 of Q^T are zero), runs the online softmax, and accumulates P.V on the VALU with the
+// probabilities broadcast through LDS.  It writes a partial (max, sum, o[4][256]) per
+// (b, kv head, chunk).
+// Phase 2 (decode_combine_kernel): per (b, query head), merges the chunk partials by
+// log-sum-exp, applies 1/l and the sigmoid gate, stores bf16 (and the fp32 LSE).
+#include "hattn_device.h"
+#include "hattn_launch.h"
+
+namespace hattn {
+
+namespace {
+
+constexpr int kStep = 32;  // keys per wave step
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  // LDS traffic of one wave is processed in order; this keeps the compiler from moving the
+  // probability stores and loads across each other.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+template <bool kSliding>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    int cap, const int* __restrict__ pos, int window, int chunk, int nchunks,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, int rope_q, RopeTable tab, float sl2) {
+  constexpr int kNdc = kSliding ? 4 : 1;  // Q fragments (32 dims each) in the first rotary half
+  __shared__ __attribute__((aligned(16))) float p_lds[kHkv][kStep][4];
+
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, kvh = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;    // MFMA view: column (head) and k-group
+  const int half = lane >> 5, dg = lane & 31;  // PV view: key parity and 8-dim group
+  const int p = pos[b];
+  int kv_len = kSliding ? min(p + 1, window) : p + 1;
+  kv_len = max(0, min(kv_len, cap));
+  const int k_begin = c * chunk;
+  const int k_end = min(kv_len, k_begin + chunk);
+
+  // Q^T operand: column n16 < 4 is query head 4*kvh + n16, dims 32dc + 8g .. +7.
+  const bool qlane = n16 < kGroup;
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = q + ((long long)b * kHq + kvh * kGroup + (qlane ? n16 : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+  }
+  if (rope_q && qlane) {
+    // Rotate-half pairs (d, d + r/2) both live in this lane: fragment dc pairs with dc + kNdc.
+#pragma unroll
+    for (int dc = 0; dc < kNdc; ++dc) {
+      const bf16x8 xa = qf[dc], xb = qf[dc + kNdc];
+      f32x4 ya0, ya1, yb0, yb1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sv, cv;
+        sincos_angle(rope_angle(p, tab.inv_freq[32 * dc + 8 * g + e]), &sv, &cv);
+        const float a = (float)xa[e], bb = (float)xb[e];
+        const float ya = a * cv - bb * sv, yb = bb * cv + a * sv;
+        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
+      }
+      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
+      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
+      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      qf[dc + kNdc] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    }
+  }
+
+  constexpr long long rs = kHkv * kD;
+  const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
+  const bf16_t* kb = kc + kv_off;
+  const bf16_t* vb = vc + kv_off;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[kGroup][8];
+#pragma unroll
+  for (int hl = 0; hl < kGroup; ++hl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
+
+  for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
+    bf16x8 kf[2][8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = k0 + 16 * blk + n16;
+      const bool ok = key < k_end;
+      const bf16_t* kr = kb + (long long)key * rs + 8 * g;
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc)
+        kf[blk][dc] = ok ? *reinterpret_cast<const bf16x8*>(kr + 32 * dc) : bf16x8{};
+    }
+    uint4 vv[16];
+#pragma unroll
+    for (int kp = 0; kp < 16; ++kp) {
+      const int key = k0 + 2 * kp + half;
+      vv[kp] = key < k_end ? *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 8 * dg)
+                           : uint4{0u, 0u, 0u, 0u};
+    }
+
+    f32x4 s[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      s[0] = mfma16(kf[0][dc], qf[dc], s[0]);
+      s[1] = mfma16(kf[1][dc], qf[dc], s[1]);
+    }
+    // s[blk][j] = score of key k0 + 16 blk + 4g + j for head column n16.
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + 16 * blk + 4 * g + j;
+        const float v = key < k_end ? s[blk][j] * sl2 : -INFINITY;
+        s[blk][j] = v;
+        mloc = fmaxf(mloc, v);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rsum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pj = fast_exp2(s[blk][j] - m_use);
+        s[blk][j] = pj;
+        rsum += pj;
+      }
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+
+    if (qlane) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p_lds[kvh][16 * blk + 4 * g + j][n16] = s[blk][j];
+    }
+    // Per-head rescale factors live in lanes 0..3 (column = head, k-group 0).
+    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
+    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
+    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[0][e] *= a0;
+      o[1][e] *= a1;
+      o[2][e] *= a2;
+      o[3][e] *= a3;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int kp = 0; kp < 16; ++kp) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(&p_lds[kvh][2 * kp + half][0]);
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vv[kp]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float v0 = bf16_lo(vw[w]), v1 = bf16_hi(vw[w]);
+#pragma unroll
+        for (int hl = 0; hl < kGroup; ++hl) {
+          o[hl][2 * w] += pv[hl] * v0;
+          o[hl][2 * w + 1] += pv[hl] * v1;
+        }
+      }
+    }
+    wave_lds_fence();
+  }
+
+  // Fold the two key parities together, then the softmax sums over the 4 k-groups.
+#pragma unroll
+  for (int hl = 0; hl < kGroup; ++hl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] += __shfl_xor(o[hl][e], 32);
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  const long long part = ((long long)(b * kHkv + kvh) * nchunks + c) * kGroup;
+  if (half == 0) {
+#pragma unroll
+    for (int hl = 0; hl < kGroup; ++hl) {
+      float* dst = ws_o + (part + hl) * kD + 8 * dg;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{o[hl][0], o[hl][1], o[hl][2], o[hl][3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[hl][4], o[hl][5], o[hl][6], o[hl][7]};
+    }
+  }
+  if (lane < kGroup) {
+    ws_ml[(part + lane) * 2] = m_run;
+    ws_ml[(part + lane) * 2 + 1] = l_run;
+  }
+}
+
+// One workgroup per (b, query head); thread d owns output dim d.
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int nchunks,
+    const bf16_t* __restrict__ gate, bf16_t* __restrict__ out, float* __restrict__ lse) {
+  const int b = blockIdx.x / kHq, h = blockIdx.x % kHq;
+  const int kvh = h / kGroup, hl = h % kGroup;
+  const int d = threadIdx.x;
+  const long long base = (long long)(b * kHkv + kvh) * nchunks;
+  float M = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ws_ml[((base + c) * kGroup + hl) * 2]);
+  const float M_use = M == -INFINITY ? 0.f : M;
+  float L = 0.f, acc = 0.f;
+  for (int c = 0; c < nchunks; ++c) {
+    const long long pc = (base + c) * kGroup + hl;
+    const float wgt = fast_exp2(ws_ml[pc * 2] - M_use);
+    L += ws_ml[pc * 2 + 1] * wgt;
+    acc += ws_o[pc * kD + d] * wgt;
+  }
+  const long long row = (long long)b * kHq + h;
+  const float g = bf16_to_f32(gate[row]);
+  const float sg = 1.f / (1.f + expf(-g));
+  const float val = L > 0.f ? acc * (sg / L) : 0.f;
+  out[row * kD + d] = f32_to_bf16(val);
+  if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int B, int max_keys) {
+  constexpr int kTargetGroups = 1024;  // about four workgroups per CU
+  const int steps = max(1, (max_keys + kStep - 1) / kStep);
+  int nchunks = max(1, min((kTargetGroups + B - 1) / B, steps));
+  const int per = (max_keys + nchunks - 1) / nchunks;
+  const int chunk = max(kStep, (per + kStep - 1) / kStep * kStep);
+  nchunks = max(1, (max_keys + chunk - 1) / chunk);
+  return DecodePlan{nchunks, chunk};
+}
+
+size_t decode_workspace_bytes(int B, const DecodePlan& plan) {
+  const size_t parts = (size_t)B * kHkv * plan.nchunks * kGroup;
+  return parts * (kD + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache, int cap,
+                         const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
+                         int window, bool rope_q, const RopeTable& tab, float scale_log2e,
+                         const DecodePlan& plan, void* workspace, hipStream_t stream) {
+  const size_t parts = (size_t)B * kHkv * plan.nchunks * kGroup;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o + parts * kD;
+  const dim3 grid((unsigned)plan.nchunks, (unsigned)B);
+  if (window > 0) {
+    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
+                       cap, pos, window, plan.chunk, plan.nchunks, ws_o, ws_ml, rope_q ? 1 : 0, tab,
+                       scale_log2e);
+  } else {
+    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
+                       cap, pos, window, plan.chunk, plan.nchunks, ws_o, ws_ml, rope_q ? 1 : 0, tab,
+                       scale_log2e);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * kHq)), dim3(256), 0, stream, ws_o,
+                     ws_ml, plan.nchunks, gate, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace hattn

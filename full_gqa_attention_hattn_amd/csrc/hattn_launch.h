@@ -1,0 +1,38 @@
+// Host-side launchers of the hattn kernels (called by the C ABI in api.hip after it has
+// validated every argument).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "hattn_device.h"
+
+namespace hattn {
+
+hipError_t launch_rope_qk(bf16_t* q, bf16_t* k, const int* pos0, int B, int S,
+                          const RopeTable& tab, hipStream_t stream);
+
+hipError_t launch_kv_append(const bf16_t* k_new, const bf16_t* v_new, bf16_t* k_cache,
+                            bf16_t* v_cache, int cap, const int* pos0, int B, int n,
+                            int window, int* slots_out, hipStream_t stream);
+
+// window == 0 selects the full-causal kernel.
+hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+                          int cap, const int* pos0, int B, int Sq, const bf16_t* gate,
+                          bf16_t* out, float* lse, int window, bool rope_q,
+                          const RopeTable& tab, float scale_log2e, hipStream_t stream);
+
+// Split-KV decode geometry, a pure function of (B, max keys per sequence).
+struct DecodePlan {
+  int nchunks;  // key chunks per sequence
+  int chunk;    // keys per chunk (multiple of 32)
+};
+DecodePlan decode_plan(int B, int max_keys);
+size_t decode_workspace_bytes(int B, const DecodePlan& plan);
+
+hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache, int cap,
+                         const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
+                         int window, bool rope_q, const RopeTable& tab, float scale_log2e,
+                         const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+}  // namespace hattn

@@ -1,0 +1,163 @@
+/*
+ * hattn -- hybrid GQA attention layer for AMD Instinct MI355X (gfx950).
+ *
+ * One attention layer of the Spark-X2.5 / X2.6-4B model family: sliding-window layers
+ * (window 512, RoPE base 1e4 over all 256 dims) and full-causal layers (RoPE base 5e6
+ * over dims 0..63, dims 64..255 unrotated), both GQA with 16 query heads over 4 KV heads,
+ * head_dim 256, softmax scale 1/16 and a per-head sigmoid output gate.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [T1] "How a million tokens fit into a 4B model: Spark X2.5's long-context
+ *        architecture and its memory trade-offs" (hotelren.com)
+ *   [T2] "No high-VRAM card needed: a 4B model takes on a million-token context"
+ *        (163.com)
+ *   [T3] "Spark-X2.6-4B-Base hybrid attention architecture" (lqnn.cn)
+ *
+ * Conventions for every call:
+ *   - All tensors are caller-owned DEVICE memory; the library allocates nothing and keeps
+ *     no state between calls except a thread-local last HIP error code.
+ *   - Activations are bf16 (raw 16-bit words), row-major "BSHD":
+ *       q, out     [B, S, 16, 256]     gate [B, S, 16]     lse [B, S, 16] fp32
+ *       k, v       [B, S, 4, 256]      caches [B, cap, 4, 256]
+ *     The element (b, s, h, d) sits at ((b*S + s)*H + h)*256 + d.
+ *   - Position arrays are int32 in device memory and are read by the kernels.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns; results are valid once the stream has reached that point.
+ *   - Arguments are validated on the host before any launch.  A call with an empty size
+ *     (no tokens or no sequences) returns HATTN_OK without looking at its pointers
+ *     (empty torch tensors carry NULL data pointers).  A non-OK status means
+ *     nothing was enqueued, except HATTN_ERR_HIP (a launch failed; see
+ *     hattn_last_hip_error).  No C++ exception crosses this interface.
+ *   - Device-side range guards: a key index outside [0, cap) is never read and a cache
+ *     slot outside [0, cap) is never written, whatever the position arrays hold.
+ *   - Calls are reentrant; calls on different streams may run concurrently as long as
+ *     they do not write the same buffers.
+ */
+#ifndef HATTN_H_
+#define HATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hattn_status;
+enum {
+  HATTN_OK = 0,
+  HATTN_ERR_NULL = 1,        /* a required pointer is NULL                             */
+  HATTN_ERR_SHAPE = 2,       /* a size is negative or too large for 32-bit indexing     */
+  HATTN_ERR_UNSUPPORTED = 3, /* heads / head_dim / rot_dim / window not the model's     */
+  HATTN_ERR_RANGE = 4,       /* cap, window or position-range rule broken               */
+  HATTN_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned                 */
+  HATTN_ERR_WORKSPACE = 6,   /* decode workspace NULL or smaller than required          */
+  HATTN_ERR_HIP = 7          /* a HIP launch failed; hattn_last_hip_error() has the code */
+};
+
+/* Layer kinds.  [T1] "Hybrid attention: only one layer in four gets the full view";
+ * [T2] "27 sliding-window layers plus 9 global layers". */
+enum { HATTN_SLIDING = 0, HATTN_FULL = 1 };
+
+/* hattn_prefill flag: q is given unrotated and the kernel applies RoPE to it in its
+ * prologue (otherwise q must already be rotated). */
+enum { HATTN_ROPE_Q_FUSED = 1u };
+
+/* Per-layer configuration.  Only the model's values are supported:
+ *   n_q_heads 16, n_kv_heads 4, head_dim 256, softmax_scale 1/16;
+ *   sliding: window 512, rot_dim 256, rope_theta 1e4;
+ *   full:    window 0,   rot_dim 64,  rope_theta 5e6.
+ * [T1] "GQA, fused projection and output gating" (heads, head_dim); [T1] "Per-layer RoPE
+ * and the local/global split" and [T3] "Global attention + 5M-base RoPE" (theta, the
+ * rotary fraction 0.25 = 64 dims); [T3] "Sliding window 512". */
+typedef struct hattn_layer_cfg {
+  int32_t kind;        /* HATTN_SLIDING or HATTN_FULL                       */
+  int32_t n_q_heads;   /* 16                                                */
+  int32_t n_kv_heads;  /* 4                                                 */
+  int32_t head_dim;    /* 256                                               */
+  int32_t window;      /* 512 for sliding, 0 for full                       */
+  int32_t rot_dim;     /* leading dims that rotate: 256 sliding, 64 full    */
+  double rope_theta;   /* 1e4 sliding, 5e6 full                             */
+  float softmax_scale; /* 1/16                                              */
+  int32_t reserved;    /* must be 0                                         */
+} hattn_layer_cfg;
+
+/* Fill *out with the preset for `kind`.  HATTN_ERR_NULL / HATTN_ERR_UNSUPPORTED. */
+hattn_status hattn_cfg_preset(int32_t kind, hattn_layer_cfg* out);
+
+/* RoPE, in place, on q [B,S,16,256] and/or k [B,S,4,256] (either may be NULL, not both).
+ * Token s of sequence b sits at position pos0[b] + s (pos0: int32 [B], device).
+ * Pair (i, i + r/2), i < r/2 with r = rot_dim, turns by angle
+ *   a = float32( float32(pos) * float32(theta ** (-2 i / r)) )
+ * (rotate-half pairing); dims r..255 are neither read nor written.  fp32 arithmetic,
+ * results rounded to bf16 (nearest-even).
+ * [T1] "Per-layer RoPE and the local/global split" (rope_parameters per layer type,
+ * compute_rope_cos_sin / apply_rotary_pos_emb); [T3] "Global attention + 5M-base RoPE". */
+hattn_status hattn_rope_qk(const hattn_layer_cfg* cfg, void* q, void* k, const int32_t* pos0,
+                           int32_t B, int32_t S, void* stream);
+
+/* Copy n rotated tokens per sequence, k_new / v_new [B,n,4,256], into the caches
+ * k_cache / v_cache [B,cap,4,256].  Token t of sequence b has position p = pos0[b] + t.
+ *   full:    slot = p; tokens with p < 0 or p >= cap are skipped (slot reported -1).
+ *   sliding: cap must equal cfg->window (the ring); slot = p mod window; when n > window
+ *            only the last `window` tokens are written (a later token would overwrite
+ *            an earlier one in the same slot), but every token's slot is reported.
+ * slots_out: int32 [B,n] device, may be NULL.
+ * [T2] "The real bottleneck of a million-token context" (sliding layers keep only the
+ * most recent 512 tokens' keys and values, full layers keep them all); [T1] "Doing the
+ * arithmetic first" (4096 bytes per token per layer). */
+hattn_status hattn_kv_append(const hattn_layer_cfg* cfg, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, int32_t cap, const int32_t* pos0,
+                             int32_t B, int32_t n, int32_t* slots_out, void* stream);
+
+/* Prefill attention for Sq query tokens per sequence.
+ *   q [B,Sq,16,256] (unrotated if flags & HATTN_ROPE_Q_FUSED, else rotated);
+ *   k_cache / v_cache [B,cap,4,256]: rotated keys and values indexed by absolute position
+ *     (row j holds the token at position j), for both layer kinds;
+ *   query i of sequence b sits at p = pos0[b] + i and sees the keys at positions
+ *     full:    0 .. p          sliding: max(0, p - window + 1) .. p
+ *     clipped to [0, cap) (callers keep pos0[b] + Sq <= cap);
+ *   gate [B,Sq,16] bf16 logits; out [B,Sq,16,256] bf16; lse [B,Sq,16] fp32 or NULL.
+ * Per (b, i, h) with kv head h/4:  s_j = (q . k_j) * softmax_scale,
+ *   out = bf16( sigmoid(gate) * sum_j softmax(s)_j v_j ),  lse = ln sum_j exp(s_j).
+ * A row with no visible key gets out = 0 and lse = -inf.
+ * [T1] "Hybrid attention" (create_causal_mask / create_sliding_window_causal_mask per layer
+ * type); [T1] "GQA, fused projection and output gating" (16 query heads share 4 KV heads;
+ * gate = sigmoid(gate_score.float()), attn_output * gate); [T2] "Grouped-query attention". */
+hattn_status hattn_prefill(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                           const void* v_cache, int32_t cap, const int32_t* pos0, int32_t B,
+                           int32_t Sq, const void* gate, void* out, float* lse, uint32_t flags,
+                           void* stream);
+
+/* Bytes of device workspace hattn_decode needs for B sequences and this cache capacity
+ * (its split-KV partial results).  0 for an invalid configuration. */
+size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap);
+
+/* Single-token decode.  q [B,1,16,256] (rotated unless flags & HATTN_ROPE_Q_FUSED),
+ * gate [B,1,16], out [B,1,16,256], lse [B,1,16] fp32 or NULL; pos: int32 [B] device,
+ * the new token's position, whose key/value must already be in the cache.
+ *   full:    k_cache / v_cache [B,cap,4,256], keys at rows 0 .. pos[b] (clipped to cap);
+ *   sliding: the ring [B,window,4,256] (cap must equal window); the first
+ *            min(pos[b] + 1, window) slots are valid (the ring is filled in position
+ *            order from position 0), and every valid slot is visible.
+ * Same arithmetic as hattn_prefill.  The key range is split into chunks whose partial
+ * (max, sum, output) triples are merged by log-sum-exp in a second kernel.
+ * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes.
+ * [T2] "The real bottleneck of a million-token context" (the ring keeps the last 512
+ * tokens); [T1] "GQA, fused projection and output gating". */
+hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                          const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
+                          const void* gate, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* Static description of a status code. */
+const char* hattn_status_string(hattn_status status);
+
+/* The hipError_t of the last HATTN_ERR_HIP on the calling thread (0 if none). */
+int32_t hattn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HATTN_H_ */

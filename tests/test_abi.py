@@ -1,0 +1,168 @@
+"""The C-ABI library loads and exports every symbol include/hattn.h declares, and its host
+argument validation returns the documented status codes.  No call here reaches a kernel
+launch (every case fails validation first or has an empty size), so this runs without a
+GPU."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "hattn.h"
+LIBPATH = ROOT / "full_gqa_attention_hattn_amd" / "libhattn.so"
+
+pytestmark = pytest.mark.skipif(not LIBPATH.exists(), reason="libhattn.so not built")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(hattn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def h():
+    from full_gqa_attention_hattn_amd import hattn
+    return hattn
+
+
+def test_exports_every_declared_symbol(h):
+    decl = declared_functions()
+    assert len(decl) >= 8
+    assert sorted(h.EXPORTS) == decl
+    lib = ctypes.CDLL(str(LIBPATH))
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_presets(h):
+    s, f = h.preset("sliding"), h.preset("full")
+    assert (s.kind, s.window, s.rot_dim, s.rope_theta) == (0, 512, 256, 1e4)
+    assert (f.kind, f.window, f.rot_dim, f.rope_theta) == (1, 0, 64, 5e6)
+    for c in (s, f):
+        assert (c.n_q_heads, c.n_kv_heads, c.head_dim, c.softmax_scale) == (16, 4, 256, 0.0625)
+    lib = h.lib()
+    assert lib.hattn_cfg_preset(7, ctypes.byref(h.LayerCfg())) == h.HATTN_ERR_UNSUPPORTED
+    assert lib.hattn_cfg_preset(0, None) == h.HATTN_ERR_NULL
+
+
+def test_status_strings(h):
+    lib = h.lib()
+    seen = set()
+    for st in range(8):
+        s = lib.hattn_status_string(st).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.hattn_status_string(99).decode() == "unknown status"
+    assert lib.hattn_last_hip_error() == 0
+
+
+P = ctypes.c_void_p
+A = P(0x10000)          # a 16-byte-aligned stand-in address (never dereferenced)
+MIS = P(0x10008)        # 8-byte aligned only
+
+
+def _cfg(h, preset_kind="full", **kw):
+    c = h.preset(preset_kind)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return ctypes.byref(c)
+
+
+@pytest.mark.parametrize("field,val", [("n_q_heads", 8), ("n_kv_heads", 8), ("head_dim", 128),
+                                       ("window", 256), ("rot_dim", 128), ("rope_theta", 1e6),
+                                       ("softmax_scale", 0.1), ("reserved", 1), ("kind", 2)])
+def test_unsupported_config(h, field, val):
+    lib = h.lib()
+    c = _cfg(h, "sliding", **{field: val})
+    assert lib.hattn_rope_qk(c, A, A, A, 1, 1, None) == h.HATTN_ERR_UNSUPPORTED
+    assert lib.hattn_prefill(c, A, A, A, 8, A, 1, 1, A, A, None, 0, None) == h.HATTN_ERR_UNSUPPORTED
+    assert lib.hattn_decode_workspace_bytes(c, 1, 512) == 0
+
+
+def test_rope_validation(h):
+    lib = h.lib()
+    c = _cfg(h)
+    assert lib.hattn_rope_qk(None, A, A, A, 1, 1, None) == h.HATTN_ERR_NULL
+    assert lib.hattn_rope_qk(c, None, None, A, 1, 1, None) == h.HATTN_ERR_NULL
+    assert lib.hattn_rope_qk(c, A, None, None, 1, 1, None) == h.HATTN_ERR_NULL
+    assert lib.hattn_rope_qk(c, A, None, A, -1, 1, None) == h.HATTN_ERR_SHAPE
+    assert lib.hattn_rope_qk(c, MIS, None, A, 1, 1, None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_rope_qk(c, None, MIS, A, 1, 1, None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_rope_qk(c, A, A, P(0x10002), 1, 1, None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_rope_qk(c, A, A, A, 0, 5, None) == h.HATTN_OK       # empty: no launch
+    assert lib.hattn_rope_qk(c, A, A, A, 3, 0, None) == h.HATTN_OK
+    assert lib.hattn_rope_qk(c, None, None, None, 0, 0, None) == h.HATTN_OK  # empty: no pointers needed
+
+
+def test_append_validation(h):
+    lib = h.lib()
+    f, s = _cfg(h, "full"), _cfg(h, "sliding")
+    ok = (A, A, A, A)
+    assert lib.hattn_kv_append(f, None, A, A, A, 8, A, 1, 1, None, None) == h.HATTN_ERR_NULL
+    assert lib.hattn_kv_append(f, *ok, 8, None, 1, 1, None, None) == h.HATTN_ERR_NULL
+    assert lib.hattn_kv_append(f, *ok, 0, A, 1, 1, None, None) == h.HATTN_ERR_SHAPE
+    assert lib.hattn_kv_append(f, *ok, 8, A, 1, -2, None, None) == h.HATTN_ERR_SHAPE
+    assert lib.hattn_kv_append(s, *ok, 511, A, 1, 1, None, None) == h.HATTN_ERR_RANGE
+    assert lib.hattn_kv_append(s, *ok, 1024, A, 1, 1, None, None) == h.HATTN_ERR_RANGE
+    assert lib.hattn_kv_append(f, A, A, MIS, A, 8, A, 1, 1, None, None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_kv_append(f, *ok, 8, A, 1, 1, P(0x10001), None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_kv_append(s, *ok, 512, A, 0, 1, None, None) == h.HATTN_OK
+    assert lib.hattn_kv_append(f, *ok, 8, A, 4, 0, None, None) == h.HATTN_OK
+
+
+def test_prefill_validation(h):
+    lib = h.lib()
+    c = _cfg(h, "sliding")
+    args = lambda **o: [o.get(k, v) for k, v in (("q", A), ("k", A), ("v", A), ("cap", 64),
+                                                   ("pos", A), ("B", 1), ("S", 8), ("g", A),
+                                                   ("out", A), ("lse", None), ("flags", 0))]
+    for k in ("q", "k", "v", "pos", "g", "out"):
+        assert lib.hattn_prefill(c, *args(**{k: None}), None) == h.HATTN_ERR_NULL, k
+    assert lib.hattn_prefill(c, *args(S=-1), None) == h.HATTN_ERR_SHAPE
+    assert lib.hattn_prefill(c, *args(cap=0), None) == h.HATTN_ERR_SHAPE
+    assert lib.hattn_prefill(c, *args(flags=6), None) == h.HATTN_ERR_UNSUPPORTED
+    for k in ("q", "k", "v", "out"):
+        assert lib.hattn_prefill(c, *args(**{k: MIS}), None) == h.HATTN_ERR_ALIGN, k
+    assert lib.hattn_prefill(c, *args(g=P(0x10001)), None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_prefill(c, *args(lse=P(0x10002)), None) == h.HATTN_ERR_ALIGN
+    assert lib.hattn_prefill(c, *args(S=0), None) == h.HATTN_OK
+    assert lib.hattn_prefill(c, *args(B=0), None) == h.HATTN_OK
+    # grid would exceed the 32-bit work-item range
+    assert lib.hattn_prefill(c, *args(B=65536, S=1 << 15), None) == h.HATTN_ERR_SHAPE
+
+
+def test_decode_validation_and_workspace(h):
+    lib = h.lib()
+    f, s = _cfg(h, "full"), _cfg(h, "sliding")
+    need = lib.hattn_decode_workspace_bytes(f, 32, 131136)
+    assert need > 0 and need % 16 == 0
+    assert lib.hattn_decode_workspace_bytes(s, 32, 512) > 0
+    assert lib.hattn_decode_workspace_bytes(s, 32, 513) == 0
+    assert lib.hattn_decode_workspace_bytes(f, -1, 8) == 0
+
+    def call(cfg=f, q=A, k=A, v=A, cap=131136, pos=A, B=32, g=A, out=A, lse=None, ws=A,
+             wsb=need, flags=0):
+        return lib.hattn_decode(cfg, q, k, v, cap, pos, B, g, out, lse, ws, wsb, flags, None)
+
+    for kw in ("q", "k", "v", "pos", "g", "out"):
+        assert call(**{kw: None}) == h.HATTN_ERR_NULL, kw
+    assert call(ws=None) == h.HATTN_ERR_WORKSPACE
+    assert call(wsb=need - 1) == h.HATTN_ERR_WORKSPACE
+    assert call(ws=MIS) == h.HATTN_ERR_ALIGN
+    assert call(cfg=s, cap=131136, wsb=1 << 40) == h.HATTN_ERR_RANGE
+    assert call(q=MIS) == h.HATTN_ERR_ALIGN
+    assert call(flags=2) == h.HATTN_ERR_UNSUPPORTED
+    assert call(B=70000, wsb=1 << 50) == h.HATTN_ERR_SHAPE
+    assert call(cap=0) == h.HATTN_ERR_SHAPE
+    assert call(B=0) == h.HATTN_OK
+
+
+def test_decode_workspace_scales_with_plan(h):
+    lib = h.lib()
+    f = _cfg(h, "full")
+    # partials: B x 4 kv heads x chunks x 4 heads x (256 + 2) floats
+    for B, cap in ((1, 1 << 20), (32, 131136), (3, 100)):
+        n = lib.hattn_decode_workspace_bytes(f, B, cap)
+        per_chunk = B * 4 * 4 * 258 * 4
+        assert n % per_chunk == 0 and n >= per_chunk

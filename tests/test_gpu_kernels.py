@@ -1,0 +1,263 @@
+"""GPU parity of every entry point against the oracle at sizes the oracle finishes in
+seconds (several tiles, ragged tails, the edge cases of the method), called through the
+C ABI.  Inputs come from `synth`; expected values only from `oracle`."""
+import math
+
+import pytest
+import torch
+
+import oracle as O
+import synth
+from parity import assert_bf16_close, check_outputs, say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["sliding", "full"]
+
+
+@pytest.fixture(scope="module")
+def h():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from full_gqa_attention_hattn_amd import hattn
+    return hattn
+
+
+def _cpu(t):
+    return t.detach().cpu()
+
+
+# ---------------------------------------------------------------------------- RoPE --
+@pytest.mark.parametrize("kind", KINDS)
+def test_rope_matches_oracle_up_to_1m_positions(h, kind):
+    say(f"rope {kind}")
+    B, S = 3, 300
+    inp = synth.layer_inputs(11, B, S, "cuda")
+    pos0 = [0, 131072 - 150, (1 << 20) - S + 1]   # last token of b=2 sits at 2^20
+    cfg = h.preset(kind)
+    q, k = inp["q"].clone(), inp["k"].clone()
+    h.rope_qk(cfg, q, k, synth.positions(pos0, B, "cuda"))
+    k2 = inp["k"].clone()
+    h.rope_qk(cfg, None, k2, synth.positions(pos0, B, "cuda"))   # K alone
+    torch.cuda.synchronize()
+    assert torch.equal(k, k2)
+    r = O.KINDS[kind].rot_dim
+    for b in range(B):
+        qr, kr = O.rope_qk(_cpu(inp["q"][b]), _cpu(inp["k"][b]), pos0[b], kind)
+        for name, g, ref, src in (("q", q[b], qr, inp["q"][b]), ("k", k[b], kr, inp["k"][b])):
+            g = _cpu(g)
+            # rotated dims: one bf16 rounding of the fp32 rotation
+            err = (g[..., :r].double() - ref[..., :r].double()).abs()
+            assert float((err - (2 ** -8) * ref[..., :r].double().abs() - 1e-5).max()) <= 0
+            exact = (g[..., :r] == ref[..., :r].to(torch.bfloat16)).double().mean()
+            assert float(exact) > 0.98, f"{name} b={b}: only {float(exact):.3f} round-to-nearest"
+            # pass-through dims untouched, bit for bit
+            assert torch.equal(g[..., r:], _cpu(src)[..., r:])
+
+
+# ---------------------------------------------------------------------- KV append --
+def test_append_full_cache_slots_and_bits(h):
+    say("append full")
+    B, n, cap = 2, 37, 200
+    cfg = h.preset("full")
+    new = synth.layer_inputs(12, B, n, "cuda")
+    cache = synth.cache_inputs(13, B, cap, cap, "cuda")
+    K, V = cache["cache_k"].clone(), cache["cache_v"].clone()
+    pos0 = [10, 180]           # second sequence runs past the capacity: those tokens skip
+    slots = torch.full((B, n), 99, dtype=torch.int32, device="cuda")
+    h.kv_append(cfg, new["k"], new["v"], K, V, synth.positions(pos0, B, "cuda"), slots)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kc, vc = _cpu(cache["cache_k"][b]).clone(), _cpu(cache["cache_v"][b]).clone()
+        ref_slots = O.kv_append(kc, vc, _cpu(new["k"][b]), _cpu(new["v"][b]), pos0[b], "full")
+        assert torch.equal(_cpu(slots[b]), ref_slots)
+        assert torch.equal(_cpu(K[b]), kc) and torch.equal(_cpu(V[b]), vc)
+    assert int((slots[1] == -1).sum()) == 180 + n - cap
+
+
+def test_append_ring_last_writer_and_slots(h):
+    say("append ring")
+    B, n = 2, 1100
+    cfg = h.preset("sliding")
+    new = synth.layer_inputs(14, B, n, "cuda")
+    cache = synth.cache_inputs(15, B, 512, 512, "cuda")
+    K, V = cache["cache_k"].clone(), cache["cache_v"].clone()
+    pos0 = [0, 131072 - 37]
+    slots = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    h.kv_append(cfg, new["k"], new["v"], K, V, synth.positions(pos0, B, "cuda"), slots)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kc, vc = _cpu(cache["cache_k"][b]).clone(), _cpu(cache["cache_v"][b]).clone()
+        ref_slots = O.kv_append(kc, vc, _cpu(new["k"][b]), _cpu(new["v"][b]), pos0[b], "sliding")
+        assert torch.equal(_cpu(slots[b]), ref_slots)
+        assert torch.equal(_cpu(K[b]), kc) and torch.equal(_cpu(V[b]), vc)
+
+
+# ------------------------------------------------------------------------ prefill --
+def _prefill_case(h, kind, B, Sq, pos0, cap, seed, fused=True, needles=()):
+    """Run rope(K) + prefill on the GPU and the oracle on the same synth inputs."""
+    cfg = h.preset(kind)
+    inp = synth.layer_inputs(seed, B, Sq, "cuda")
+    cache = synth.cache_inputs(seed + 1, B, cap, cap, "cuda")
+    K_src, V = cache["cache_k"], cache["cache_v"]
+    q_src = inp["q"]
+    for (b, i, j, dims) in needles:
+        synth.plant_needle(q_src, K_src, b, i, j, dims, 16.0)
+    K = K_src.clone()
+    h.rope_qk(cfg, None, K, synth.positions(0, B, "cuda"))      # cache rows are positions 0..cap-1
+    q = q_src.clone()
+    if not fused:
+        h.rope_qk(cfg, q, None, synth.positions(pos0, B, "cuda"))
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Sq, 16, dtype=torch.float32, device="cuda")
+    h.prefill(cfg, q, K, V, synth.positions(pos0, B, "cuda"), inp["gate"], out, lse,
+              rope_q_fused=fused)
+    torch.cuda.synchronize()
+    refs = []
+    for b in range(B):
+        _, kr = O.rope_qk(None, _cpu(K_src[b]), 0, kind)
+        y, l = O.prefill(_cpu(q_src[b]), kr, _cpu(V[b]), _cpu(inp["gate"][b]), pos0[b], kind)
+        refs.append((y, l))
+    return out, lse, refs, inp, V
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("fused", [True, False])
+def test_prefill_tiny_config(h, kind, fused):
+    """The tiny workload: B=1, S=1024, positions 0..1023, every output element."""
+    say(f"prefill tiny {kind} fused={fused}")
+    out, lse, refs, _, _ = _prefill_case(h, kind, 1, 1024, [0], 1024, 21, fused)
+    check_outputs(out[0], lse[0], refs[0][0], refs[0][1], f"tiny {kind} fused={fused}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_prefill_ragged_offsets(h, kind):
+    """Ragged query count (not a multiple of the 32-row block), per-sequence start
+    positions, and a cache capacity that is not a multiple of the 64-key tile."""
+    say(f"prefill ragged {kind}")
+    B, Sq, cap = 2, 777, 1500
+    pos0 = [0, 700]
+    out, lse, refs, _, _ = _prefill_case(h, kind, B, Sq, pos0, cap, 31)
+    for b in range(B):
+        check_outputs(out[b], lse[b], refs[b][0], refs[b][1], f"ragged {kind} b={b}")
+
+
+@pytest.mark.parametrize("Sq", [1, 31, 33, 64, 65])
+def test_prefill_small_shapes(h, Sq):
+    say(f"prefill small Sq={Sq}")
+    for kind in KINDS:
+        out, lse, refs, _, _ = _prefill_case(h, kind, 1, Sq, [5], Sq + 5, 41 + Sq)
+        check_outputs(out[0], lse[0], refs[0][0], refs[0][1], f"Sq={Sq} {kind}")
+
+
+def test_prefill_needles_window_edge(h):
+    """A planted key with logit ~32 owns the output of its row when visible (distance 511
+    on a sliding layer; distance ~1.2K on a full layer) and is ignored at distance 512."""
+    say("prefill needles")
+    S = 1400
+    # sliding: dims (127, 255) turn slowest; full: dims 128 and 200 do not rotate
+    cases = [("sliding", (0, 1300, 1300 - 511, (127, 255)), True),
+             ("sliding", (0, 1200, 1200 - 512, (127, 255)), False),
+             ("full", (0, 1399, 3, (128, 200)), True)]
+    for kind, nd, seen in cases:
+        out, lse, refs, inp, V = _prefill_case(h, kind, 1, S, [0], S, 51, needles=[nd])
+        b, i, j, _ = nd
+        check_outputs(out[0], lse[0], refs[0][0], refs[0][1], f"needle {kind} seen={seen}")
+        for hq in range(16):
+            sig = 1 / (1 + math.exp(-float(inp["gate"][b, i, hq])))
+            target = _cpu(V[b, j, hq // 4]).double() * sig
+            err = float((_cpu(out[b, i, hq]).double() - target).norm() / target.norm())
+            assert (err < 2e-2) if seen else (err > 0.5), (kind, hq, err)
+
+
+def test_prefill_deterministic(h):
+    say("prefill determinism")
+    cfg = h.preset("full")
+    inp = synth.layer_inputs(61, 1, 600, "cuda")
+    pos0 = synth.positions(0, 1, "cuda")
+    outs = []
+    for _ in range(2):
+        o = torch.empty_like(inp["q"])
+        h.prefill(cfg, inp["q"], inp["k"], inp["v"], pos0, inp["gate"], o, None)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_empty_sizes_are_noops(h):
+    cfg = h.preset("sliding")
+    q = torch.zeros(1, 0, 16, 256, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 0, 4, 256, dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(1, 0, 16, dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros(1, 512, 4, 256, dtype=torch.bfloat16, device="cuda")
+    pos = synth.positions(0, 1, "cuda")
+    h.rope_qk(cfg, q, k, pos)
+    h.kv_append(cfg, k, k, K, K.clone(), pos)
+    h.prefill(cfg, q, K, K, pos, g, q.clone(), None)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------- decode --
+def _decode_case(h, kind, positions, cap, seed, fused):
+    cfg = h.preset(kind)
+    B = len(positions)
+    new = synth.layer_inputs(seed, B, 1, "cuda")
+    cache = synth.cache_inputs(seed + 1, B, cap, cap, "cuda")
+    K, V = cache["cache_k"], cache["cache_v"]
+    q = new["q"].clone()
+    pos = synth.positions(positions, B, "cuda")
+    if not fused:
+        h.rope_qk(cfg, q, None, pos)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
+    ws = h.alloc_workspace(cfg, B, cap)
+    h.decode(cfg, q, K, V, pos, new["gate"], out, lse, ws, rope_q_fused=fused)
+    torch.cuda.synchronize()
+    for b, p in enumerate(positions):
+        y, l = O.decode(_cpu(new["q"][b, 0]), _cpu(K[b]), _cpu(V[b]), _cpu(new["gate"][b, 0]),
+                        p, kind)
+        check_outputs(out[b, 0], lse[b, 0], y, l, f"decode {kind} p={p} fused={fused}")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_full_cache(h, fused):
+    say(f"decode full fused={fused}")
+    _decode_case(h, "full", [0, 31, 777, 1999, 4999], 5000, 71, fused)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_ring(h, fused):
+    say(f"decode ring fused={fused}")
+    _decode_case(h, "sliding", [0, 5, 510, 511, 512, 131072, (1 << 20)], 512, 81, fused)
+
+
+def test_decode_equals_prefill_row(h):
+    """Cross-path: decoding the token at position p equals prefill row p."""
+    say("decode == prefill row")
+    for kind in KINDS:
+        cfg = h.preset(kind)
+        S = 900
+        inp = synth.layer_inputs(91, 1, S, "cuda")
+        pos0 = synth.positions(0, 1, "cuda")
+        K = inp["k"].clone()
+        h.rope_qk(cfg, None, K, pos0)
+        out = torch.empty_like(inp["q"])
+        lse = torch.empty(1, S, 16, dtype=torch.float32, device="cuda")
+        h.prefill(cfg, inp["q"], K, inp["v"], pos0, inp["gate"], out, lse)
+        for p in (0, 511, 512, S - 1):
+            if kind == "full":
+                Kc, Vc, cap = K, inp["v"], S
+            else:   # build the ring the way a decoder would: append positions 0..p
+                Kc = torch.zeros(1, 512, 4, 256, dtype=torch.bfloat16, device="cuda")
+                Vc = torch.zeros_like(Kc)
+                h.kv_append(cfg, K[:, :p + 1], inp["v"][:, :p + 1], Kc, Vc, pos0)
+                cap = 512
+            q = inp["q"][:, p:p + 1].contiguous()
+            od = torch.empty_like(q)
+            ld = torch.empty(1, 1, 16, dtype=torch.float32, device="cuda")
+            ws = h.alloc_workspace(cfg, 1, cap)
+            h.decode(cfg, q, Kc, Vc, synth.positions(p, 1, "cuda"),
+                     inp["gate"][:, p:p + 1].contiguous(), od, ld, ws, rope_q_fused=True)
+            torch.cuda.synchronize()
+            assert_bf16_close(od[0, 0], out[0, p].float(), f"{kind} p={p}", atol=4e-3, rtol=1e-2)
+            assert float((ld[0, 0] - lse[0, p]).abs().max()) < 1e-3
