@@ -14,8 +14,8 @@
 // 4..15 of Q^T are zero), runs the online softmax, and accumulates P.V on the VALU with the
 // probabilities broadcast through LDS.  It writes a partial (max, sum, o[4][256]) per
 // (b, kv head, chunk).
-// Phase 2 (decode_combine_kernel): per (b, query head), merges the chunk partials by
-// log-sum-exp, applies 1/l and the sigmoid gate, stores bf16 (and the fp32 LSE).
+// Phase 2 (decode_combine_kernel): per (b, query head, 32-dim slice), merges the chunk
+// partials by log-sum-exp, applies 1/l and the sigmoid gate, stores bf16 (and the LSE).
 #include "hattn_device.h"
 #include "hattn_launch.h"
 
@@ -208,30 +208,57 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
-// One workgroup per (b, query head); thread d owns output dim d.
+// Grid (B * 16 query heads, 256 / 32 dim slices); 256 threads = 32 dims x 8 chunk groups.
+// Pass 1: the largest chunk max.  Pass 2: each chunk group folds every 8th chunk's partial
+// with weight 2^(m_c - M); the 8 groups are summed through LDS.
+constexpr int kCombDims = 32;
+constexpr int kCombGroups = 8;
+
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int nchunks,
     const bf16_t* __restrict__ gate, bf16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float red_o[kCombGroups][kCombDims];
+  __shared__ float red_l[kCombGroups];
+  __shared__ float red_m[4];
   const int b = blockIdx.x / kHq, h = blockIdx.x % kHq;
   const int kvh = h / kGroup, hl = h % kGroup;
-  const int d = threadIdx.x;
+  const int dl = threadIdx.x & (kCombDims - 1), cg = threadIdx.x / kCombDims;
+  const int d = blockIdx.y * kCombDims + dl;
   const long long base = (long long)(b * kHkv + kvh) * nchunks;
+
   float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ws_ml[((base + c) * kGroup + hl) * 2]);
+  for (int c = threadIdx.x; c < nchunks; c += 256) M = fmaxf(M, ws_ml[((base + c) * kGroup + hl) * 2]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((threadIdx.x & 63) == 0) red_m[threadIdx.x >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   const float M_use = M == -INFINITY ? 0.f : M;
+
   float L = 0.f, acc = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
+#pragma unroll 4
+  for (int c = cg; c < nchunks; c += kCombGroups) {
     const long long pc = (base + c) * kGroup + hl;
     const float wgt = fast_exp2(ws_ml[pc * 2] - M_use);
     L += ws_ml[pc * 2 + 1] * wgt;
     acc += ws_o[pc * kD + d] * wgt;
   }
-  const long long row = (long long)b * kHq + h;
-  const float g = bf16_to_f32(gate[row]);
-  const float sg = 1.f / (1.f + expf(-g));
-  const float val = L > 0.f ? acc * (sg / L) : 0.f;
-  out[row * kD + d] = f32_to_bf16(val);
-  if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  red_o[cg][dl] = acc;
+  if (dl == 0) red_l[cg] = L;
+  __syncthreads();
+  if (cg == 0) {
+    float Lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < kCombGroups; ++g2) {
+      Lt += red_l[g2];
+      at += red_o[g2][dl];
+    }
+    const long long row = (long long)b * kHq + h;
+    const float g = bf16_to_f32(gate[row]);
+    const float sg = 1.f / (1.f + expf(-g));
+    out[row * kD + d] = f32_to_bf16(Lt > 0.f ? at * (sg / Lt) : 0.f);
+    if (d == 0 && lse != nullptr) lse[row] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -270,8 +297,8 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * kHq)), dim3(256), 0, stream, ws_o,
-                     ws_ml, plan.nchunks, gate, out, lse);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * kHq), kD / kCombDims), dim3(256), 0,
+                     stream, ws_o, ws_ml, plan.nchunks, gate, out, lse);
   return hipGetLastError();
 }
 

@@ -13,14 +13,16 @@
 //   * wave w owns query head 4*kvh + w, so every K/V tile staged in LDS feeds all 4 heads
 //     of its group;
 //   * S^T = K . Q^T and O^T = V^T . P^T run on v_mfma_f32_32x32x16_bf16 with fp32
-//     accumulation: a lane holds one query row's scores, so the online-softmax max/sum
-//     need one cross-lane exchange (lane ^ 32) and the rescale of O is lane-local;
-//   * P^T goes from the score accumulators to the PV MFMA in registers: V^T is written to
-//     LDS with its keys in the order a lane's accumulator holds them;
-//   * K and V^T tiles (64 keys) are double-buffered in XOR-swizzled LDS (conflict-free
-//     16-byte MFMA operand reads), loaded one tile ahead through registers;
+//     accumulation; a lane holds one query row's scores, so the online-softmax max needs
+//     one cross-lane exchange (lane ^ 32) and the rescale of O is lane-local;
+//   * K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
+//     registers), row-major with an XOR swizzle of the 16-byte blocks; the V^T operand is
+//     read with ds_read_b64_tr_b16, which transposes 4 keys x 16 dims per lane group, in
+//     the key order in which a lane already holds P^T in its score accumulator;
+//   * the row max used for exp2 only moves when a tile beats it by more than 2^8, so O is
+//     rescaled rarely (probabilities stay <= 256 in between, exact in fp32 and bf16 range);
 //   * tiles wholly outside the causal / sliding band are never visited; only tiles that
-//     straddle the band edge or the diagonal evaluate the element mask;
+//     straddle the band edge, the diagonal or the cache end evaluate the element mask;
 //   * optional fused Q-RoPE: the workgroup computes cos/sin of its 32 positions once into
 //     LDS and each lane rotates its own Q fragment (pairs d, d + r/2 sit in the same lane);
 //   * epilogue: 1/l, sigmoid gate, bf16 store, optional fp32 LSE.
@@ -31,98 +33,56 @@ namespace hattn {
 
 namespace {
 
-constexpr int kBQ = 32;                   // query positions per workgroup
-constexpr int kBN = 64;                   // keys per tile
-constexpr int kThreads = 256;             // 4 waves
-constexpr int kKBytes = kBN * kD * 2;     // K tile: 64 rows x 512 B
-constexpr int kVBytes = kD * kBN * 2;     // V^T tile: 256 rows x 128 B
-constexpr int kStage = kKBytes + kVBytes;
-constexpr int kLds = 2 * kStage;
+constexpr int kBQ = 32;                  // query positions per workgroup
+constexpr int kThreads = 256;            // 4 waves
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleLog2 = 8.f;      // move the running max only when beaten by 2^8
 
-// K tile: key row r, 16-byte block c (dims 8c..8c+7) at r*512 + ((c ^ (r & 7)) << 4).
-__device__ __forceinline__ int k_off(int r, int c) { return r * 512 + ((c ^ (r & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void g_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// V^T tile: dim row d, 16-byte block c (8 key slots) at d*128 + ((c ^ swz(d)) << 4).
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-__device__ __forceinline__ int vt_off(int d, int c) { return d * 128 + ((c ^ vt_swz(d)) << 4); }
-
-// Slot of key kl (0..15) inside its 16-key chunk of a V^T row.  Lane half hh of the score
-// accumulator holds, per 16-key chunk, keys 4hh..4hh+3 then 8+4hh..8+4hh+3; those land in
-// slots 8hh..8hh+7, which is what that lane half reads as the PV operand.
-__device__ __forceinline__ int v_slot(int kl) {
-  return ((kl >> 2) & 1) * 8 + (kl >> 3) * 4 + (kl & 3);
-}
+// LDS tile row (one key, 512 bytes): 16-byte block b sits at block b ^ swz(r).  swz is a
+// permutation of 0..7 over r & 7, so the 16-byte K reads of 8 consecutive rows hit 8
+// different bank groups, and the 8-byte transposed V reads of 4 consecutive rows (aligned
+// to 4) land in 4 disjoint block pairs.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int tile_off(int r, int b) { return r * 512 + ((b ^ swz(r)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-struct TileRegs {
-  uint4 k[8];
-  uint4 v[8];
-};
-
-// Global -> registers for the 64-key tile starting at key0.  Rows at or past `cap` read as
-// zero and are never dereferenced.
-__device__ __forceinline__ void load_tile(TileRegs& R, const bf16_t* kbase, const bf16_t* vbase,
-                                          int key0, int cap, int tid) {
+// Issue this wave's share of a kBN-row tile load straight into LDS.  Instruction i of wave
+// w fills LDS bytes [(nw*w + i)*1024, +1024): lane l's 16 bytes land at position
+// (nw*w + i)*64 + l, i.e. row p/32, physical block p%32, so it fetches the logical block
+// that the swizzle maps there.  Rows at or past `cap` read row cap-1 instead; their scores
+// are masked to -inf, so their values never reach the output.
+template <int kBN>
+__device__ __forceinline__ void load_tile_lds(char* dst, const bf16_t* base, int key0, int cap,
+                                              int w, int lane) {
+  constexpr int nw = kBN / 8;  // wave-instructions per wave per tile (4 waves)
   constexpr long long rs = kHkv * kD;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int item = it * kThreads + tid;  // 2048 16-byte blocks
-    const int r = item >> 5, c = item & 31;
-    const int key = key0 + r;
-    R.k[it] = key < cap ? *reinterpret_cast<const uint4*>(kbase + key * rs + c * 8)
-                        : uint4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int item = it * kThreads + tid;  // 512 items of 4 keys x 8 dims
-    const int dg = item & 31, kg = item >> 5;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + kg * 4 + r;
-      R.v[it * 4 + r] = key < cap ? *reinterpret_cast<const uint4*>(vbase + key * rs + dg * 8)
-                                  : uint4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < nw; ++i) {
+    const int p = (nw * w + i) * 64 + lane;
+    const int r = p >> 5;
+    const int lb = (p & 31) ^ swz(r);
+    const int key = min(key0 + r, cap - 1);
+    __builtin_amdgcn_global_load_lds(
+        (g_void*)(base + key * rs + lb * 8), (lds_void*)(dst + (nw * w + i) * 1024), 16, 0, 0);
   }
 }
 
-// Registers -> LDS stage: K as is (swizzled), V transposed 4 keys x 8 dims per item.
-__device__ __forceinline__ void store_tile(const TileRegs& R, char* kst, char* vst, int tid) {
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int item = it * kThreads + tid;
-    const int r = item >> 5, c = item & 31;
-    *reinterpret_cast<uint4*>(kst + k_off(r, c)) = R.k[it];
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int item = it * kThreads + tid;
-    const int dg = item & 31, kg = item >> 5;
-    const int kl0 = kg * 4;
-    const int e_idx = (kl0 >> 4) * 16 + v_slot(kl0 & 15);  // 4 consecutive slots
-    const int blk = e_idx >> 3, byte = (e_idx & 7) * 2;
-    const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&R.v[it * 4 + 0]);
-    const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&R.v[it * 4 + 1]);
-    const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&R.v[it * 4 + 2]);
-    const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&R.v[it * 4 + 3]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int d = dg * 8 + 2 * w;
-      const uint2 lo{__builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u),
-                     __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u)};
-      const uint2 hi{__builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u),
-                     __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u)};
-      *reinterpret_cast<uint2*>(vst + vt_off(d, blk) + byte) = lo;
-      *reinterpret_cast<uint2*>(vst + vt_off(d + 1, blk) + byte) = hi;
-    }
-  }
+__device__ __forceinline__ void wait_lds_dma() {
+  // vmcnt(0): this wave's global->LDS copies have landed (expcnt/lgkmcnt left alone).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <bool kSliding>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool kSliding, int kBN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBN == 64 ? 1 : 2, 2)))
 void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
                     const bf16_t* __restrict__ vc, int cap, const int* __restrict__ pos0, int B,
                     int Sq, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
@@ -130,7 +90,10 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
                     int nqb, int nwork) {
   constexpr int kHalf = kSliding ? 128 : 32;  // rot_dim / 2
   constexpr int kNdc = kHalf / 16;           // Q fragments holding the first rotary half
-  __shared__ __attribute__((aligned(16))) char smem[kLds];
+  constexpr int kTile = kBN * kD * 2;        // bytes of one K or V tile
+  constexpr int kStage = 2 * kTile;
+  constexpr int kKB = kBN / 32;              // 32-key blocks per tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -138,8 +101,8 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 
   int qb, b, kvh;
   if (kSliding) {
-    // Equal work per workgroup: give each XCD (blockIdx % 8) a contiguous run of query
-    // blocks so the K/V tiles that neighbouring blocks share stay in that XCD's L2.
+    // Equal work per workgroup: each XCD (blockIdx % 8) gets a contiguous run of query
+    // blocks, so the K/V tiles that neighbouring blocks share stay in that XCD's L2.
     const int per = (int)(gridDim.x >> 3);
     const int logical = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
     if (logical >= nwork) return;
@@ -164,6 +127,15 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const bool row_ok = n < nrows;
   const int row_i = i0 + (row_ok ? n : 0);
   const int prow = P0 + n;
+
+  const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
+  const bf16_t* kbase = kc + kv_off;
+  const bf16_t* vbase = vc + kv_off;
+  const int kmax = min(Plast, cap - 1);
+  const int kmin = kSliding ? max(0, P0 - (window - 1)) : 0;
+  const bool any_keys = kmax >= kmin;
+  const int t_lo = any_keys ? kmin / kBN : 0;
+  const int t_hi = any_keys ? kmax / kBN : -1;
 
   // Q^T operand: lane (n, hh) holds dims 16dc + 8hh .. +7 of query row n.
   bf16x8 qf[16];
@@ -206,108 +178,121 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     __syncthreads();  // the cos/sin table shares LDS with the first tile
   }
 
-  const int kmax = min(Plast, cap - 1);
-  const int kmin = kSliding ? max(0, P0 - (window - 1)) : 0;
+  // Per-lane LDS address parts that do not depend on the tile.
+  // K operand (S^T = K Q^T): row 32kb + n, block 2dc + hh.
+  const int ksw = swz(n);
+  // V^T operand via ds_read_b64_tr_b16: within 16-lane group g = lane/16, lane i supplies
+  // the 8 bytes at key 4hh + i/4 (+16c, +8 for the second half), dims 16(g&1) + 4(i&3)
+  // (+32mb); the instruction hands lane i the 4 keys of dim 16(g&1) + i.
+  const int gi = lane & 15;
+  const int trow = 4 * hh + (gi >> 2);
+  const int tdim = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+  const int tsw = swz(trow);
+  const int tlo = (tdim & 7) * 2;  // 0 or 8 bytes into the 16-byte block
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
 
-  const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
-  const bf16_t* kbase = kc + kv_off;
-  const bf16_t* vbase = vc + kv_off;
-
-  if (kmax >= kmin) {
-    const int t_lo = kmin / kBN, t_hi = kmax / kBN;
-    TileRegs R;
-    load_tile(R, kbase, vbase, t_lo * kBN, cap, tid);
-    store_tile(R, smem, smem + kKBytes, tid);
+  if (any_keys) {
+    load_tile_lds<kBN>(smem, kbase, t_lo * kBN, cap, w, lane);
+    load_tile_lds<kBN>(smem + kTile, vbase, t_lo * kBN, cap, w, lane);
+    wait_lds_dma();
     __syncthreads();
-    for (int t = t_lo; t <= t_hi; ++t) {
-      const char* kst = smem + ((t - t_lo) & 1) * kStage;
-      const char* vst = kst + kKBytes;
-      const bool more = t < t_hi;
-      if (more) load_tile(R, kbase, vbase, (t + 1) * kBN, cap, tid);
+  }
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const char* kst = smem + ((t - t_lo) & 1) * kStage;
+    const char* vst = kst + kTile;
+    if (t < t_hi) {
+      char* nk = smem + ((t + 1 - t_lo) & 1) * kStage;
+      load_tile_lds<kBN>(nk, kbase, (t + 1) * kBN, cap, w, lane);
+      load_tile_lds<kBN>(nk + kTile, vbase, (t + 1) * kBN, cap, w, lane);
+    }
 
-      // S^T[key][query] for keys 0..31 (s0) and 32..63 (s1) of the tile.
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // S^T[key][query]; accumulator element 4i + j of lane half hh in block kb is key
+    // 32kb + 8i + 4hh + j of the tile.
+    f32x16 s[kKB];
 #pragma unroll
-      for (int dc = 0; dc < 16; ++dc) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kst + k_off(n, 2 * dc + hh));
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kst + k_off(32 + n, 2 * dc + hh));
-        s0 = mfma32(a0, qf[dc], s0);
-        s1 = mfma32(a1, qf[dc], s1);
+    for (int kb = 0; kb < kKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < 16; ++dc) {
+      const int blk = ((2 * dc + hh) & 7) ^ ksw;
+      const int off = (dc >> 2) * 128 + (blk << 4);
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + (32 * kb + n) * 512 + off);
+        s[kb] = mfma32(a, qf[dc], s[kb]);
       }
+    }
 
-      // Accumulator element 4i + j of lane half hh is key 8i + 4hh + j (+32 for s1).
-      const int key0 = t * kBN;
-      const bool whole = (key0 + kBN - 1 <= P0) && (key0 + kBN <= cap) &&
-                         (!kSliding || Plast - key0 <= window - 1);
-      float mloc = -INFINITY;
+    const int key0 = t * kBN;
+    const bool whole = (key0 + kBN - 1 <= P0) && (key0 + kBN <= cap) &&
+                       (!kSliding || Plast - key0 <= window - 1);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float a = s0[idx] * sl2, c = s1[idx] * sl2;
+        float v = s[kb][idx] * sl2;
         if (!whole) {
-          const int j0 = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
-          const int j1 = j0 + 32;
-          const bool v0 = j0 <= prow && j0 < cap && (!kSliding || prow - j0 <= window - 1);
-          const bool v1 = j1 <= prow && j1 < cap && (!kSliding || prow - j1 <= window - 1);
-          a = v0 ? a : -INFINITY;
-          c = v1 ? c : -INFINITY;
+          const int j = key0 + 32 * kb + 8 * (idx >> 2) + 4 * hh + (idx & 3);
+          const bool vis = j <= prow && j < cap && (!kSliding || prow - j <= window - 1);
+          v = vis ? v : -INFINITY;
         }
-        s0[idx] = a;
-        s1[idx] = c;
-        mloc = fmaxf(mloc, fmaxf(a, c));
+        s[kb][idx] = v;
+        mloc = fmaxf(mloc, v);
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
+    // first visible key); otherwise probabilities stay below 256 and O is left alone.
+    const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
+    if (__any(bump)) {
       const float m_new = fmaxf(m_run, mloc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        s0[idx] = fast_exp2(s0[idx] - m_use);
-        s1[idx] = fast_exp2(s1[idx] - m_use);
-        rs += s0[idx] + s1[idx];
+        const float pv = fast_exp2(s[kb][idx] - m_use);
+        s[kb][idx] = pv;
+        rs += pv;
       }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
-      }
+    }
+    l_run += rs;
 
-      // P^T operands, one per 16-key chunk, straight from the accumulators.
-      bf16x8 pf[4];
-      {
-        const f32x4 c0 = {s0[0], s0[1], s0[2], s0[3]}, c1 = {s0[4], s0[5], s0[6], s0[7]};
-        const f32x4 c2 = {s0[8], s0[9], s0[10], s0[11]}, c3 = {s0[12], s0[13], s0[14], s0[15]};
-        const f32x4 c4 = {s1[0], s1[1], s1[2], s1[3]}, c5 = {s1[4], s1[5], s1[6], s1[7]};
-        const f32x4 c6 = {s1[8], s1[9], s1[10], s1[11]}, c7 = {s1[12], s1[13], s1[14], s1[15]};
-        const bf16x4 b0 = __builtin_convertvector(c0, bf16x4), b1 = __builtin_convertvector(c1, bf16x4);
-        const bf16x4 b2 = __builtin_convertvector(c2, bf16x4), b3 = __builtin_convertvector(c3, bf16x4);
-        const bf16x4 b4 = __builtin_convertvector(c4, bf16x4), b5 = __builtin_convertvector(c5, bf16x4);
-        const bf16x4 b6 = __builtin_convertvector(c6, bf16x4), b7 = __builtin_convertvector(c7, bf16x4);
-        pf[0] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        pf[1] = bf16x8{b2[0], b2[1], b2[2], b2[3], b3[0], b3[1], b3[2], b3[3]};
-        pf[2] = bf16x8{b4[0], b4[1], b4[2], b4[3], b5[0], b5[1], b5[2], b5[3]};
-        pf[3] = bf16x8{b6[0], b6[1], b6[2], b6[3], b7[0], b7[1], b7[2], b7[3]};
-      }
+    // P^T operands, one per 16-key chunk c: accumulator elements 8(c%2) .. +7 of block c/2.
+#pragma unroll
+    for (int c = 0; c < 2 * kKB; ++c) {
+      const f32x16& sc = s[c >> 1];
+      const int e0 = 8 * (c & 1);
+      const f32x4 lo = {sc[e0], sc[e0 + 1], sc[e0 + 2], sc[e0 + 3]};
+      const f32x4 hi = {sc[e0 + 4], sc[e0 + 5], sc[e0 + 6], sc[e0 + 7]};
+      const bf16x4 pl = __builtin_convertvector(lo, bf16x4);
+      const bf16x4 ph = __builtin_convertvector(hi, bf16x4);
+      const bf16x8 pf = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vst + vt_off(32 * mb + n, 2 * c + hh));
-          o[mb] = mfma32(a, pf[c], o[mb]);
-        }
+        const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
+        const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        o[mb] = mfma32(a, pf, o[mb]);
       }
-
-      if (more) {
-        char* nk = smem + ((t + 1 - t_lo) & 1) * kStage;
-        store_tile(R, nk, nk + kKBytes, tid);
-      }
-      __syncthreads();
     }
+
+    if (t < t_hi) wait_lds_dma();
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -333,6 +318,11 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   }
 }
 
+#ifndef HATTN_PREFILL_BN
+#define HATTN_PREFILL_BN 32
+#endif
+constexpr int kBNSel = HATTN_PREFILL_BN;
+
 }  // namespace
 
 hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache, int cap,
@@ -343,13 +333,13 @@ hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* 
   const long long nwork = (long long)B * kHkv * nqb;
   if (window > 0) {
     const long long grid = (nwork + 7) / 8 * 8;
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, q,
-                       k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse, window, rope_q ? 1 : 0,
-                       tab, scale_log2e, nqb, (int)nwork);
+    hipLaunchKernelGGL((prefill_kernel<true, kBNSel>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse, window,
+                       rope_q ? 1 : 0, tab, scale_log2e, nqb, (int)nwork);
   } else {
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)nwork), dim3(kThreads), 0, stream, q,
-                       k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse, window, rope_q ? 1 : 0,
-                       tab, scale_log2e, nqb, (int)nwork);
+    hipLaunchKernelGGL((prefill_kernel<false, kBNSel>), dim3((unsigned)nwork), dim3(kThreads), 0,
+                       stream, q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse, window,
+                       rope_q ? 1 : 0, tab, scale_log2e, nqb, (int)nwork);
   }
   return hipGetLastError();
 }
