@@ -307,17 +307,41 @@ def _sha(path):
 
 
 def measured_traffic(kernel_src: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary (profiles/traffic_<workload>.txt, "key: value" lines), or None when that
+    file is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
     src = os.path.join(ROOT, "full_gqa_attention_hattn_amd", "csrc", kernel_src)
     if rec.get("source_sha256") != _sha(src):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    """One plain device-to-device copy of `mib` MiB (outside the timed region), so a
+    counter pass over this run also records FETCH_SIZE / WRITE_SIZE for a copy of known
+    size, which calibrates those counters to bytes."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 # ------------------------------------------------------------------------------ main --
@@ -329,6 +353,9 @@ def main():
     ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the workload "
+                         "(for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
@@ -338,6 +365,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
 
+    copy_calibration(args.copy_calibration_mib)
     wl = make_workload(args.workload)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
