@@ -9,21 +9,22 @@
 // gating" (16 query heads share 4 KV heads; sigmoid gate multiplied into each head's
 // output); [T2] "Grouped-query attention"; [T3] "Sliding window 512".
 //
-// Design (one workgroup = 4 waves = one KV head x 32 query positions):
-//   * wave w owns query head 4*kvh + w, so every K/V tile staged in LDS feeds all 4 heads
-//     of its group;
+// Design (one workgroup = one KV head x 32 or 64 query positions, 4 or 8 waves):
+//   * wave w owns query head 4*kvh + w%4 and one 32-row block, so every K/V tile staged in
+//     LDS feeds all 4 heads of its group (and both row blocks when 8 waves share it);
 //   * S^T = K . Q^T and O^T = V^T . P^T run on v_mfma_f32_32x32x16_bf16 with fp32
 //     accumulation; a lane holds one query row's scores, so the online-softmax max needs
 //     one cross-lane exchange (lane ^ 32) and the rescale of O is lane-local;
-//   * K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
-//     registers), row-major with an XOR swizzle of the 16-byte blocks; the V^T operand is
-//     read with ds_read_b64_tr_b16, which transposes 4 keys x 16 dims per lane group, in
-//     the key order in which a lane already holds P^T in its score accumulator;
+//   * 32-key K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
+//     registers), double-buffered, row-major with an XOR swizzle of the 16-byte blocks; the
+//     V^T operand is read with ds_read_b64_tr_b16, which transposes 4 keys x 16 dims per
+//     lane group, in the key order in which a lane already holds P^T in its accumulator;
 //   * the row max used for exp2 only moves when a tile beats it by more than 2^8, so O is
 //     rescaled rarely (probabilities stay <= 256 in between, exact in fp32 and bf16 range);
-//   * tiles wholly outside the causal / sliding band are never visited; only tiles that
-//     straddle the band edge, the diagonal or the cache end evaluate the element mask;
-//   * optional fused Q-RoPE: the workgroup computes cos/sin of its 32 positions once into
+//   * tiles wholly outside the causal / sliding band are never visited (per workgroup, and
+//     per wave for the row blocks of an 8-wave group); only tiles that straddle the band
+//     edge, the diagonal or the cache end evaluate the element mask;
+//   * optional fused Q-RoPE: the workgroup computes cos/sin of its positions once into
 //     LDS and each lane rotates its own Q fragment (pairs d, d + r/2 sit in the same lane);
 //   * epilogue: 1/l, sigmoid gate, bf16 store, optional fp32 LSE.
 #include "hattn_device.h"
@@ -33,8 +34,7 @@ namespace hattn {
 
 namespace {
 
-constexpr int kBQ = 32;                  // query positions per workgroup
-constexpr int kThreads = 256;            // 4 waves
+constexpr int kBN = 32;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleLog2 = 8.f;      // move the running max only when beaten by 2^8
 
@@ -44,60 +44,68 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// LDS tile row (one key, 512 bytes): 16-byte block b sits at block b ^ swz(r).  swz is a
-// permutation of 0..7 over r & 7, so the 16-byte K reads of 8 consecutive rows hit 8
-// different bank groups, and the 8-byte transposed V reads of 4 consecutive rows (aligned
-// to 4) land in 4 disjoint block pairs.
+// LDS tile row (one key, 512 bytes): 16-byte block b sits at block b ^ swz(r), a
+// permutation of 0..7 over r & 7.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int tile_off(int r, int b) { return r * 512 + ((b ^ swz(r)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Issue this wave's share of a kBN-row tile load straight into LDS.  Instruction i of wave
-// w fills LDS bytes [(nw*w + i)*1024, +1024): lane l's 16 bytes land at position
-// (nw*w + i)*64 + l, i.e. row p/32, physical block p%32, so it fetches the logical block
-// that the swizzle maps there.  Rows at or past `cap` read row cap-1 instead; their scores
-// are masked to -inf, so their values never reach the output.
-template <int kBN>
+// Issue this wave's share of a 32-row tile load straight into LDS.  The tile is 16 KiB =
+// 16 wave-instructions of 1 KiB; wave w issues instructions w*nw .. w*nw + nw - 1.
+// Instruction j fills LDS bytes [j*1024, +1024): lane l's 16 bytes land at position
+// p = j*64 + l, i.e. row p/32, physical block p%32, so it fetches the logical block the
+// swizzle maps there.  Rows at or past `cap` read row cap-1 instead; their scores are
+// masked to -inf, so their values never reach the output.
+template <int kWaves>
 __device__ __forceinline__ void load_tile_lds(char* dst, const bf16_t* base, int key0, int cap,
                                               int w, int lane) {
-  constexpr int nw = kBN / 8;  // wave-instructions per wave per tile (4 waves)
+  constexpr int nw = 16 / kWaves;
   constexpr long long rs = kHkv * kD;
 #pragma unroll
   for (int i = 0; i < nw; ++i) {
-    const int p = (nw * w + i) * 64 + lane;
+    const int j = nw * w + i;
+    const int p = j * 64 + lane;
     const int r = p >> 5;
     const int lb = (p & 31) ^ swz(r);
     const int key = min(key0 + r, cap - 1);
-    __builtin_amdgcn_global_load_lds(
-        (g_void*)(base + key * rs + lb * 8), (lds_void*)(dst + (nw * w + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((g_void*)(base + key * rs + lb * 8),
+                                     (lds_void*)(dst + j * 1024), 16, 0, 0);
   }
 }
 
+// Wait until at most n of this wave's global->LDS copies are still in flight.
+template <int n>
 __device__ __forceinline__ void wait_lds_dma() {
-  // vmcnt(0): this wave's global->LDS copies have landed (expcnt/lgkmcnt left alone).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
-template <bool kSliding, int kBN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBN == 64 ? 1 : 2, 2)))
+template <bool kSliding, int kWaves, int kStages>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
                     const bf16_t* __restrict__ vc, int cap, const int* __restrict__ pos0, int B,
                     int Sq, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
                     float* __restrict__ lse, int window, int rope_q, RopeTable tab, float sl2,
                     int nqb, int nwork) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kRB = kWaves / kGroup;       // 32-row blocks per workgroup
+  constexpr int kBQ = 32 * kRB;              // query positions per workgroup
   constexpr int kHalf = kSliding ? 128 : 32;  // rot_dim / 2
   constexpr int kNdc = kHalf / 16;           // Q fragments holding the first rotary half
   constexpr int kTile = kBN * kD * 2;        // bytes of one K or V tile
   constexpr int kStage = 2 * kTile;
-  constexpr int kKB = kBN / 32;              // 32-key blocks per tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  constexpr int kPitch = kHalf + 2;          // cos/sin table row, f32x2; +16 B vs bank aliasing
+  constexpr int kCsBytes = kBQ * kPitch * 8;
+  constexpr int kLdsBytes = kStages * kStage > kCsBytes ? kStages * kStage : kCsBytes;
+  constexpr int kLoadsPerTile = 2 * (16 / kWaves);  // K and V wave-instructions per wave
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
+  const int rb = w / kGroup;                 // this wave's row block
 
   int qb, b, kvh;
   if (kSliding) {
@@ -119,14 +127,18 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     kvh = rest % kHkv;
     b = rest / kHkv;
   }
-  const int h = kvh * kGroup + w;
+  const int h = kvh * kGroup + (w % kGroup);
   const int i0 = qb * kBQ;
   const int nrows = min(kBQ, Sq - i0);
   const int P0 = pos0[b] + i0;
   const int Plast = P0 + nrows - 1;
-  const bool row_ok = n < nrows;
-  const int row_i = i0 + (row_ok ? n : 0);
-  const int prow = P0 + n;
+  // This wave's rows: 32rb .. 32rb + 31 of the workgroup.
+  const int r0 = 32 * rb;
+  const bool row_ok = r0 + n < nrows;
+  const int row_i = i0 + (row_ok ? r0 + n : 0);
+  const int prow = P0 + r0 + n;
+  const int Pw0 = P0 + r0;                           // first row position of this wave
+  const int Pwl = P0 + min(r0 + 31, nrows - 1);      // last valid row position of this wave
 
   const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
   const bf16_t* kbase = kc + kv_off;
@@ -136,8 +148,11 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const bool any_keys = kmax >= kmin;
   const int t_lo = any_keys ? kmin / kBN : 0;
   const int t_hi = any_keys ? kmax / kBN : -1;
+  // Tiles this wave's rows can see at all (a workgroup's row blocks see different bands).
+  const int wt_lo = kSliding ? max(0, Pw0 - (window - 1)) / kBN : 0;
+  const int wt_hi = min(Pwl, cap - 1) / kBN;
 
-  // Q^T operand: lane (n, hh) holds dims 16dc + 8hh .. +7 of query row n.
+  // Q^T operand: lane (n, hh) holds dims 16dc + 8hh .. +7 of query row n of this wave.
   bf16x8 qf[16];
   {
     const bf16_t* qrow = q + (((long long)b * Sq + row_i) * kHq + h) * kD + 8 * hh;
@@ -148,7 +163,6 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   }
 
   if (rope_q) {
-    constexpr int kPitch = kHalf + 2;  // f32x2 per row; +16 B breaks LDS bank aliasing
     f32x2* cs = reinterpret_cast<f32x2*>(smem);
     for (int e = tid; e < kBQ * kHalf; e += kThreads) {
       const int r = e / kHalf, f = e - r * kHalf;
@@ -159,7 +173,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     __syncthreads();
 #pragma unroll
     for (int dc = 0; dc < kNdc; ++dc) {
-      const f32x2* c8 = cs + n * kPitch + 16 * dc + 8 * hh;
+      const f32x2* c8 = cs + (r0 + n) * kPitch + 16 * dc + 8 * hh;
       const bf16x8 xa = qf[dc], xb = qf[dc + kNdc];
       f32x4 ya0, ya1, yb0, yb1;
 #pragma unroll
@@ -175,12 +189,11 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
       qf[dc + kNdc] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
     }
-    __syncthreads();  // the cos/sin table shares LDS with the first tile
+    __syncthreads();  // the cos/sin table shares LDS with the first tiles
   }
 
   // Per-lane LDS address parts that do not depend on the tile.
-  // K operand (S^T = K Q^T): row 32kb + n, block 2dc + hh.
-  const int ksw = swz(n);
+  const int ksw = swz(n);  // K operand: row n, block 2dc + hh
   // V^T operand via ds_read_b64_tr_b16: within 16-lane group g = lane/16, lane i supplies
   // the 8 bytes at key 4hh + i/4 (+16c, +8 for the second half), dims 16(g&1) + 4(i&3)
   // (+32mb); the instruction hands lane i the 4 keys of dim 16(g&1) + i.
@@ -195,103 +208,105 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
 
-  if (any_keys) {
-    load_tile_lds<kBN>(smem, kbase, t_lo * kBN, cap, w, lane);
-    load_tile_lds<kBN>(smem + kTile, vbase, t_lo * kBN, cap, w, lane);
-    wait_lds_dma();
-    __syncthreads();
-  }
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const char* kst = smem + ((t - t_lo) & 1) * kStage;
-    const char* vst = kst + kTile;
-    if (t < t_hi) {
-      char* nk = smem + ((t + 1 - t_lo) & 1) * kStage;
-      load_tile_lds<kBN>(nk, kbase, (t + 1) * kBN, cap, w, lane);
-      load_tile_lds<kBN>(nk + kTile, vbase, (t + 1) * kBN, cap, w, lane);
+  // Prologue: tiles t_lo .. t_lo + kStages - 2 in flight.
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) {
+    const int t = t_lo + i;
+    if (t <= t_hi) {
+      char* st = smem + (i % kStages) * kStage;
+      load_tile_lds<kWaves>(st, kbase, t * kBN, cap, w, lane);
+      load_tile_lds<kWaves>(st + kTile, vbase, t * kBN, cap, w, lane);
     }
+  }
+  if (t_lo + kStages - 2 <= t_hi) wait_lds_dma<kLoadsPerTile * (kStages - 2)>();
+  else wait_lds_dma<0>();
+  __syncthreads();
 
-    // S^T[key][query]; accumulator element 4i + j of lane half hh in block kb is key
-    // 32kb + 8i + 4hh + j of the tile.
-    f32x16 s[kKB];
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int dc = 0; dc < 16; ++dc) {
-      const int blk = ((2 * dc + hh) & 7) ^ ksw;
-      const int off = (dc >> 2) * 128 + (blk << 4);
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + (32 * kb + n) * 512 + off);
-        s[kb] = mfma32(a, qf[dc], s[kb]);
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int it = t - t_lo;
+    const char* kst = smem + (it % kStages) * kStage;
+    const char* vst = kst + kTile;
+    {
+      const int tn = t + kStages - 1;  // refill the stage read during the previous tile
+      if (tn <= t_hi) {
+        char* st = smem + ((it + kStages - 1) % kStages) * kStage;
+        load_tile_lds<kWaves>(st, kbase, tn * kBN, cap, w, lane);
+        load_tile_lds<kWaves>(st + kTile, vbase, tn * kBN, cap, w, lane);
       }
     }
 
-    const int key0 = t * kBN;
-    const bool whole = (key0 + kBN - 1 <= P0) && (key0 + kBN <= cap) &&
-                       (!kSliding || Plast - key0 <= window - 1);
-    float mloc = -INFINITY;
+    if (t >= wt_lo && t <= wt_hi) {
+      // S^T[key][query]; accumulator element 4i + j of lane half hh is key 8i + 4hh + j.
+      f32x16 s = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
+      for (int dc = 0; dc < 16; ++dc) {
+        const int blk = ((2 * dc + hh) & 7) ^ ksw;
+        const int off = (dc >> 2) * 128 + (blk << 4);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + n * 512 + off);
+        s = mfma32(a, qf[dc], s);
+      }
+
+      const int key0 = t * kBN;
+      const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= cap) &&
+                         (!kSliding || Pwl - key0 <= window - 1);
+      float mloc = -INFINITY;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float v = s[kb][idx] * sl2;
+        float v = s[idx] * sl2;
         if (!whole) {
-          const int j = key0 + 32 * kb + 8 * (idx >> 2) + 4 * hh + (idx & 3);
+          const int j = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
           const bool vis = j <= prow && j < cap && (!kSliding || prow - j <= window - 1);
           v = vis ? v : -INFINITY;
         }
-        s[kb][idx] = v;
+        s[idx] = v;
         mloc = fmaxf(mloc, v);
       }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
-    // first visible key); otherwise probabilities stay below 256 and O is left alone.
-    const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
-    if (__any(bump)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
+      // first visible key); otherwise probabilities stay below 256 and O is left alone.
+      const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
+      if (__any(bump)) {
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
+        for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float rs = 0.f;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        const float pv = fast_exp2(s[kb][idx] - m_use);
-        s[kb][idx] = pv;
+        const float pv = fast_exp2(s[idx] - m_use);
+        s[idx] = pv;
         rs += pv;
       }
-    }
-    l_run += rs;
+      l_run += rs;
 
-    // P^T operands, one per 16-key chunk c: accumulator elements 8(c%2) .. +7 of block c/2.
+      // O^T += V^T P^T, one 16-key chunk c at a time: P^T is accumulator elements 8c .. 8c+7.
 #pragma unroll
-    for (int c = 0; c < 2 * kKB; ++c) {
-      const f32x16& sc = s[c >> 1];
-      const int e0 = 8 * (c & 1);
-      const f32x4 lo = {sc[e0], sc[e0 + 1], sc[e0 + 2], sc[e0 + 3]};
-      const f32x4 hi = {sc[e0 + 4], sc[e0 + 5], sc[e0 + 6], sc[e0 + 7]};
-      const bf16x4 pl = __builtin_convertvector(lo, bf16x4);
-      const bf16x4 ph = __builtin_convertvector(hi, bf16x4);
-      const bf16x8 pf = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
+      for (int c = 0; c < 2; ++c) {
+        const f32x4 lo = {s[8 * c], s[8 * c + 1], s[8 * c + 2], s[8 * c + 3]};
+        const f32x4 hi = {s[8 * c + 4], s[8 * c + 5], s[8 * c + 6], s[8 * c + 7]};
+        const bf16x4 pl = __builtin_convertvector(lo, bf16x4);
+        const bf16x4 ph = __builtin_convertvector(hi, bf16x4);
+        const bf16x8 pf = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
-        const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-        o[mb] = mfma32(a, pf, o[mb]);
+        for (int mb = 0; mb < 8; ++mb) {
+          const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
+          const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+          o[mb] = mfma32(a, pf, o[mb]);
+        }
       }
     }
 
-    if (t < t_hi) wait_lds_dma();
+    // Tile t + 1 must have landed before the barrier; later tiles may stay in flight.
+    if (t + kStages - 1 <= t_hi) wait_lds_dma<kLoadsPerTile * (kStages - 2)>();
+    else wait_lds_dma<0>();
     __syncthreads();
   }
 
@@ -318,10 +333,28 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   }
 }
 
-#ifndef HATTN_PREFILL_BN
-#define HATTN_PREFILL_BN 32
-#endif
-constexpr int kBNSel = HATTN_PREFILL_BN;
+// Launch shapes, measured on MI355X: full-causal rows stream long K/V prefixes, so 8 waves
+// (two 32-row blocks per head) share each staged tile and halve L2 requests; sliding rows
+// see a 512-key band, where 32-row blocks waste fewer keys at the band edges.
+constexpr int kWavesFull = 8;
+constexpr int kWavesSliding = 4;
+constexpr int kStagesSel = 2;  // K/V tiles resident in LDS
+
+template <bool kSliding, int kWaves>
+hipError_t launch_kind(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache, int cap,
+                       const int* pos0, int B, int Sq, const bf16_t* gate, bf16_t* out,
+                       float* lse, int window, bool rope_q, const RopeTable& tab,
+                       float scale_log2e, hipStream_t stream) {
+  constexpr int kBQ = 32 * (kWaves / kGroup);
+  const int nqb = (Sq + kBQ - 1) / kBQ;
+  const long long nwork = (long long)B * kHkv * nqb;
+  // Sliding grids are padded to a multiple of 8 for the XCD-contiguous mapping.
+  const long long grid = kSliding ? (nwork + 7) / 8 * 8 : nwork;
+  hipLaunchKernelGGL((prefill_kernel<kSliding, kWaves, kStagesSel>), dim3((unsigned)grid),
+                     dim3(64 * kWaves), 0, stream, q, k_cache, v_cache, cap, pos0, B, Sq, gate,
+                     out, lse, window, rope_q ? 1 : 0, tab, scale_log2e, nqb, (int)nwork);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -329,19 +362,11 @@ hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* 
                           const int* pos0, int B, int Sq, const bf16_t* gate, bf16_t* out,
                           float* lse, int window, bool rope_q, const RopeTable& tab,
                           float scale_log2e, hipStream_t stream) {
-  const int nqb = (Sq + kBQ - 1) / kBQ;
-  const long long nwork = (long long)B * kHkv * nqb;
-  if (window > 0) {
-    const long long grid = (nwork + 7) / 8 * 8;
-    hipLaunchKernelGGL((prefill_kernel<true, kBNSel>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       stream, q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse, window,
-                       rope_q ? 1 : 0, tab, scale_log2e, nqb, (int)nwork);
-  } else {
-    hipLaunchKernelGGL((prefill_kernel<false, kBNSel>), dim3((unsigned)nwork), dim3(kThreads), 0,
-                       stream, q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse, window,
-                       rope_q ? 1 : 0, tab, scale_log2e, nqb, (int)nwork);
-  }
-  return hipGetLastError();
+  if (window > 0)
+    return launch_kind<true, kWavesSliding>(q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse,
+                                            window, rope_q, tab, scale_log2e, stream);
+  return launch_kind<false, kWavesFull>(q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse,
+                                        window, rope_q, tab, scale_log2e, stream);
 }
 
 }  // namespace hattn
