@@ -52,28 +52,43 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Issue this wave's share of a 32-row tile load straight into LDS.  The tile is 16 KiB =
-// 16 wave-instructions of 1 KiB; wave w issues instructions w*nw .. w*nw + nw - 1.
+// This wave's share of a 32-row tile load straight into LDS.  The tile is 16 KiB = 16
+// wave-instructions of 1 KiB; wave w issues instructions w*nw .. w*nw + nw - 1.
 // Instruction j fills LDS bytes [j*1024, +1024): lane l's 16 bytes land at position
 // p = j*64 + l, i.e. row p/32, physical block p%32, so it fetches the logical block the
-// swizzle maps there.  Rows at or past `cap` read row cap-1 instead; their scores are
-// masked to -inf, so their values never reach the output.
+// swizzle maps there.  The per-lane source offsets (bytes from the tile's first row) do not
+// depend on the tile, so they are computed once; the tile base is wave-uniform.
 template <int kWaves>
-__device__ __forceinline__ void load_tile_lds(char* dst, const bf16_t* base, int key0, int cap,
-                                              int w, int lane) {
-  constexpr int nw = 16 / kWaves;
-  constexpr long long rs = kHkv * kD;
+struct TileLoader {
+  static constexpr int nw = 16 / kWaves;
+  static constexpr int kRowBytes = kHkv * kD * 2;  // cache row stride (4 KV heads)
+  int lrow[nw];   // tile row each load instruction of this lane reads
+  int lblk[nw];   // logical 16-byte block within that row
+
+  __device__ __forceinline__ TileLoader(int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < nw; ++i) {
-    const int j = nw * w + i;
-    const int p = j * 64 + lane;
-    const int r = p >> 5;
-    const int lb = (p & 31) ^ swz(r);
-    const int key = min(key0 + r, cap - 1);
-    __builtin_amdgcn_global_load_lds((g_void*)(base + key * rs + lb * 8),
-                                     (lds_void*)(dst + j * 1024), 16, 0, 0);
+    for (int i = 0; i < nw; ++i) {
+      const int p = (nw * w + i) * 64 + lane;
+      lrow[i] = p >> 5;
+      lblk[i] = (p & 31) ^ swz(p >> 5);
+    }
   }
-}
+
+  // Rows at or past `cap` read row cap-1 instead; their scores are masked to -inf, so
+  // their values never reach the output.
+  __device__ __forceinline__ void load(char* dst, const bf16_t* base, int key0, int cap,
+                                       int w) const {
+    const char* tile = reinterpret_cast<const char*>(base) + (long long)key0 * kRowBytes;
+    const bool tail = key0 + kBN > cap;
+#pragma unroll
+    for (int i = 0; i < nw; ++i) {
+      const int r = tail ? min(lrow[i], cap - 1 - key0) : lrow[i];
+      const unsigned off = (unsigned)r * kRowBytes + (unsigned)lblk[i] * 16u;
+      __builtin_amdgcn_global_load_lds((g_void*)(tile + off),
+                                       (lds_void*)(dst + (nw * w + i) * 1024), 16, 0, 0);
+    }
+  }
+};
 
 // Wait until at most n of this wave's global->LDS copies are still in flight.
 template <int n>
@@ -207,6 +222,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   f32x16 o[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
+  const TileLoader<kWaves> ld(w, lane);
 
   // Prologue: tiles t_lo .. t_lo + kStages - 2 in flight.
 #pragma unroll
@@ -214,8 +230,8 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     const int t = t_lo + i;
     if (t <= t_hi) {
       char* st = smem + (i % kStages) * kStage;
-      load_tile_lds<kWaves>(st, kbase, t * kBN, cap, w, lane);
-      load_tile_lds<kWaves>(st + kTile, vbase, t * kBN, cap, w, lane);
+      ld.load(st, kbase, t * kBN, cap, w);
+      ld.load(st + kTile, vbase, t * kBN, cap, w);
     }
   }
   if (t_lo + kStages - 2 <= t_hi) wait_lds_dma<kLoadsPerTile * (kStages - 2)>();
@@ -230,36 +246,52 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       const int tn = t + kStages - 1;  // refill the stage read during the previous tile
       if (tn <= t_hi) {
         char* st = smem + ((it + kStages - 1) % kStages) * kStage;
-        load_tile_lds<kWaves>(st, kbase, tn * kBN, cap, w, lane);
-        load_tile_lds<kWaves>(st + kTile, vbase, tn * kBN, cap, w, lane);
+        ld.load(st, kbase, tn * kBN, cap, w);
+        ld.load(st + kTile, vbase, tn * kBN, cap, w);
       }
     }
 
     if (t >= wt_lo && t <= wt_hi) {
       // S^T[key][query]; accumulator element 4i + j of lane half hh is key 8i + 4hh + j.
+      // K fragments are read two ahead of the MFMA that consumes them.
+      auto kfrag = [&](int dc) {
+        const int blk = ((2 * dc + hh) & 7) ^ ksw;
+        return *reinterpret_cast<const bf16x8*>(kst + n * 512 + (dc >> 2) * 128 + (blk << 4));
+      };
       f32x16 s = f32x16{};
+      bf16x8 ka = kfrag(0), kb = kfrag(1);
 #pragma unroll
       for (int dc = 0; dc < 16; ++dc) {
-        const int blk = ((2 * dc + hh) & 7) ^ ksw;
-        const int off = (dc >> 2) * 128 + (blk << 4);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + n * 512 + off);
-        s = mfma32(a, qf[dc], s);
+        const bf16x8 kn = dc + 2 < 16 ? kfrag(dc + 2) : kb;
+        s = mfma32(ka, qf[dc], s);
+        ka = kb;
+        kb = kn;
       }
+      // Keep two LDS reads in flight ahead of the MFMA chain.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
       const int key0 = t * kBN;
       const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= cap) &&
                          (!kSliding || Pwl - key0 <= window - 1);
+      if (!whole) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          const int j = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
+          const bool vis = j <= prow && j < cap && (!kSliding || prow - j <= window - 1);
+          s[idx] = vis ? s[idx] : -INFINITY;
+        }
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float v = s[idx] * sl2;
-        if (!whole) {
-          const int j = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
-          const bool vis = j <= prow && j < cap && (!kSliding || prow - j <= window - 1);
-          v = vis ? v : -INFINITY;
-        }
-        s[idx] = v;
-        mloc = fmaxf(mloc, v);
+        s[idx] *= sl2;
+        mloc = fmaxf(mloc, s[idx]);
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
@@ -283,25 +315,41 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       }
       l_run += rs;
 
-      // O^T += V^T P^T, one 16-key chunk c at a time: P^T is accumulator elements 8c .. 8c+7.
+      // O^T += V^T P^T.  P^T of 16-key chunk c is accumulator elements 8c .. 8c+7.
+      bf16x8 pf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const f32x4 lo = {s[8 * c], s[8 * c + 1], s[8 * c + 2], s[8 * c + 3]};
         const f32x4 hi = {s[8 * c + 4], s[8 * c + 5], s[8 * c + 6], s[8 * c + 7]};
         const bf16x4 pl = __builtin_convertvector(lo, bf16x4);
         const bf16x4 ph = __builtin_convertvector(hi, bf16x4);
-        const bf16x8 pf = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
-          const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-          o[mb] = mfma32(a, pf, o[mb]);
-        }
+        pf[c] = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
       }
+      // V^T fragment i = 8c + mb: keys 16c + trow (slots 0..3) and 16c + 8 + trow (slots
+      // 4..7), dims 32mb + 16(g&1) + ..; read one MFMA ahead of its use.
+      auto vfrag = [&](int i) {
+        const int c = i >> 3, mb = i & 7;
+        const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
+        const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
+        return __builtin_bit_cast(bf16x8,
+                                  s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      };
+      bf16x8 va = vfrag(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bf16x8 vn = i + 1 < 16 ? vfrag(i + 1) : va;
+        o[i & 7] = mfma32(va, pf[i >> 3], o[i & 7]);
+        va = vn;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
     }
 
     // Tile t + 1 must have landed before the barrier; later tiles may stay in flight.
