@@ -223,6 +223,9 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
   const TileLoader<kWaves> ld(w, lane);
+  // The two waves sharing a SIMD (row blocks 0 and 1 of one head) would otherwise reach
+  // their softmax phases together; issue priority for row block 0 staggers them.
+  if (rb == 0) __builtin_amdgcn_s_setprio(2);
 
   // Prologue: tiles t_lo .. t_lo + kStages - 2 in flight.
 #pragma unroll
@@ -287,13 +290,11 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
           s[idx] = vis ? s[idx] : -INFINITY;
         }
       }
+      // Row max of the raw scores, then scaled (sl2 > 0 commutes with max).
       float mloc = -INFINITY;
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        s[idx] *= sl2;
-        mloc = fmaxf(mloc, s[idx]);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      for (int idx = 0; idx < 16; ++idx) mloc = fmaxf(mloc, s[idx]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
       // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
       // first visible key); otherwise probabilities stay below 256 and O is left alone.
       const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
@@ -309,7 +310,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       float rs = 0.f;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        const float pv = fast_exp2(s[idx] - m_use);
+        const float pv = fast_exp2(__builtin_fmaf(s[idx], sl2, -m_use));
         s[idx] = pv;
         rs += pv;
       }
