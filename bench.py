@@ -287,8 +287,8 @@ def cpu_baseline(wl, budget_s: float):
     for b in range(wl.B):
         kc = L["K"][b, :wl.p].cpu()
         vc = L["V"][b, :wl.p].cpu()
-        _, kn = O.rope_qk(None, L["k_src"][b], wl.p, "full")
-        kc = torch.cat([kc.to(torch.float32), kn.cpu()])
+        _, kn = O.rope_qk(None, L["k_src"][b].cpu(), wl.p, "full")
+        kc = torch.cat([kc.to(torch.float32), kn])
         vc = torch.cat([vc.to(torch.float32), L["v"][b].cpu().to(torch.float32)])
         O.decode(L["q"][b, 0].cpu(), kc, vc, L["gate"][b, 0].cpu(), wl.p, "full")
         nbytes += KV_BYTES_PER_TOKEN * (wl.p + 1)

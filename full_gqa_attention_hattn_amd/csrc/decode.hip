@@ -264,7 +264,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 }  // namespace
 
 DecodePlan decode_plan(int B, int max_keys) {
-  constexpr int kTargetGroups = 1024;  // about four workgroups per CU
+  // One resident round: the split kernel's ~224 VGPRs leave room for two 4-wave workgroups
+  // per CU, 512 on the 256-CU chip.  A second, partly filled round costs more than the
+  // longer chunks do (measured at B = 1 with 2^20 keys and at B = 32 with 131073).
+  constexpr int kTargetGroups = 512;
   const int steps = max(1, (max_keys + kStep - 1) / kStep);
   int nchunks = max(1, min((kTargetGroups + B - 1) / B, steps));
   const int per = (max_keys + nchunks - 1) / nchunks;
