@@ -247,6 +247,30 @@ def prefill(q, k_cache, v_cache, gate, pos0: int, kind, *, q_rotated: bool = Fal
                   row_block=row_block)
 
 
+def prefill_ring(q, k_new, v_new, k_ring, v_ring, gate, pos0: int, *,
+                 q_rotated: bool = False, rows=None, row_block: int = 64):
+    """One sequence's sliding-layer prefill of a chunk that continues a ring cache.
+    The chunk's n tokens sit at positions pos0 .. pos0 + n - 1: q [n, Hq, D] (unrotated
+    unless q_rotated), gate [n, Hq], and their rotated keys / values k_new, v_new
+    [n, Hkv, D].  k_ring / v_ring [WINDOW, Hkv, D] hold the keys / values of positions
+    0 .. pos0 - 1 appended in order, so slot s holds ring_positions(pos0 - 1)[s].
+    A query at p sees the positions p - 511 .. p: the older ones come from the ring, the
+    rest from the chunk.  [T2] "The real bottleneck of a million-token context" (a
+    sliding layer keeps only the last 512 tokens' keys and values); [T3] "Sliding window
+    512".  Returns y [len(rows), Hq, D] fp64 and lse [len(rows), Hq] fp64."""
+    n = q.shape[0]
+    idx = torch.arange(n, dtype=torch.int64) if rows is None else torch.as_tensor(rows, dtype=torch.int64)
+    q_pos = idx + pos0
+    qs = q[idx]
+    q_rot = qs.to(torch.float32) if q_rotated else rope_rotate(qs, q_pos, "sliding")
+    held = ring_positions(pos0 - 1) if pos0 > 0 else torch.full((WINDOW,), -1, dtype=torch.int64)
+    keep = held >= 0
+    k_pos = torch.cat([held[keep], torch.arange(n, dtype=torch.int64) + pos0])
+    kc = torch.cat([k_ring[keep].to(torch.float32), k_new.to(torch.float32)])
+    vc = torch.cat([v_ring[keep].to(torch.float32), v_new.to(torch.float32)])
+    return attend(q_rot, kc, vc, gate[idx], q_pos, k_pos, "sliding", row_block=row_block)
+
+
 def decode(q, k_cache, v_cache, gate, pos: int, kind, *, q_rotated: bool = False):
     """One new token of one sequence at position pos (already appended).  q [Hq, D],
     gate [Hq].  Full layers: the cache holds positions 0..pos at slots 0..pos.  Sliding
@@ -303,7 +327,8 @@ __all__ = [
     "N_Q_HEADS", "N_KV_HEADS", "HEAD_DIM", "SOFTMAX_SCALE", "WINDOW", "N_LAYERS",
     "LayerKind", "SLIDING", "FULL", "KINDS", "kind_of", "layer_schedule",
     "rope_inv_freq", "rope_angles", "rope_rotate", "visible", "sigmoid64", "attend",
-    "rope_qk", "append_slots", "kv_append", "ring_positions", "prefill", "decode",
+    "rope_qk", "append_slots", "kv_append", "ring_positions", "prefill", "prefill_ring",
+    "decode",
     "kv_bytes_per_token_layer", "kv_cache_bytes", "attention_pairs_prefill",
     "sdpa_flops_per_pair",
 ]

@@ -381,6 +381,59 @@ def test_decode_equals_prefill_row_and_ring_equals_window(kind):
     assert torch.allclose(yd, yp[0], atol=1e-6) and torch.allclose(ld, lp[0], atol=1e-6)
 
 
+def test_ring_chunks_equal_one_shot_prefill():
+    """Prefilling a sequence chunk by chunk, each chunk reading the ring that the previous
+    chunks filled, gives the rows of one prefill over a position-indexed cache.  The ring
+    starts as NaN, so reading a slot that no token has reached would poison the result."""
+    S, cuts = 1337, [0, 100, 700, 733, 1337]   # chunks of 100, 600, 33 and 604 tokens
+    base = synth.layer_inputs(79, 1, S)
+    q, k, v, g = (base[n][0] for n in ("q", "k", "v", "gate"))
+    _, kr = O.rope_qk(None, k, 0, "sliding")
+    kr = kr.to(torch.bfloat16)
+    y1, l1 = O.prefill(q, kr, v, g, 0, "sliding")
+    ring_k = torch.full((512, 4, 256), float("nan"), dtype=torch.bfloat16)
+    ring_v = torch.full_like(ring_k, float("nan"))
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        yc, lc = O.prefill_ring(q[a:b], kr[a:b], v[a:b], ring_k, ring_v, g[a:b], a)
+        assert torch.allclose(yc, y1[a:b], atol=1e-6, rtol=0), (a, b)
+        assert torch.allclose(lc, l1[a:b], atol=1e-9, rtol=0), (a, b)
+        O.kv_append(ring_k, ring_v, kr[a:b], v[a:b], a, "sliding")
+
+
+def test_ring_prefill_brute_force_slot_lookup():
+    """Naive per-(row, head, key) evaluation that locates each visible position by
+    scanning the ring for the slot holding it, at a chunk that starts past one wrap."""
+    pos0, n = 530, 3
+    base = synth.layer_inputs(80, 1, pos0 + n)
+    q, k, v, g = (base[nm][0] for nm in ("q", "k", "v", "gate"))
+    _, kr = O.rope_qk(None, k, 0, "sliding")
+    kr = kr.to(torch.bfloat16)
+    ring_k = torch.zeros(512, 4, 256, dtype=torch.bfloat16)
+    ring_v = torch.zeros_like(ring_k)
+    for t in range(pos0):           # ring state after appending positions 0 .. pos0 - 1
+        ring_k[t % 512], ring_v[t % 512] = kr[t], v[t]
+    y, lse = O.prefill_ring(q[pos0:], kr[pos0:], v[pos0:], ring_k, ring_v, g[pos0:], pos0)
+    qr, _ = O.rope_qk(q[pos0:], None, pos0, "sliding")
+    for i in range(n):
+        p = pos0 + i
+        for h in range(16):
+            scores, vals = [], []
+            for j in range(max(0, p - 511), p + 1):
+                if j >= pos0:
+                    kj, vj = kr[j], v[j]
+                else:
+                    slot = [s for s in range(512) if s == j % 512 and j >= pos0 - 512][0]
+                    kj, vj = ring_k[slot], ring_v[slot]
+                kh = kj[h // 4].double().numpy()
+                scores.append(float(np.dot(qr[i, h].double().numpy(), kh)) / 16.0)
+                vals.append(vj[h // 4].double().numpy())
+            sc = np.array(scores)
+            w = np.exp(sc - sc.max())
+            ref = (w[:, None] * np.stack(vals)).sum(0) / w.sum() / (1 + math.exp(-float(g[p, h])))
+            assert np.allclose(y[i, h].numpy(), ref, atol=1e-5, rtol=1e-5)
+            assert abs(float(lse[i, h]) - (sc.max() + math.log(w.sum()))) < 1e-5
+
+
 # ------------------------------------------------------------------ closed forms --
 def test_kv_memory_matches_page_figures():
     m = json.loads((GOLD / "kv_memory.json").read_text())
