@@ -8,8 +8,9 @@ split-KV partials and their log-sum-exp combine).
 
 Default workload (the 1M-context full layer, B=1): a cache holding positions
 0..1044479, a chunked prefill of 4096 queries at positions 1044480..1048575, then one
-decode at position 1048576 over 1048577 keys.  Other workloads (--workload 2|3|4) are
-the 32K sliding prefill, the 128K full prefill and the B=32 mixed decode at 128K.
+decode at position 1048576 over 1048577 keys.  Other workloads (--workload 2|3|4|6) are
+the 32K sliding prefill, the 128K full prefill, the B=32 mixed decode at 128K and the
+sliding-layer side of the 1M chunk (prefill against the 512-slot ring, append, decode).
 
 Prints one JSON line.  `value` is the prefill attention throughput of the whole step
 (algorithmic prefill FLOP / step time); the decode KV bandwidth and per-kernel rates,
@@ -221,6 +222,60 @@ class Full1MWorkload:
                      self.ws, rope_q_fused=True)
 
 
+class SlidingRing1MWorkload:
+    """Workload 6: the sliding-layer side of the 1M-context chunk, B=1 -- a chunk prefill
+    that continues a full 512-slot ring, the chunk's append into the ring, then one
+    ring decode."""
+
+    def __init__(self, device="cuda"):
+        from full_gqa_attention_hattn_amd import hattn
+        self.h = hattn
+        W = synth.WORKLOADS[6]
+        self.W = W
+        self.P, self.C, self.pd = W.params["ring_pos"], W.params["chunk"], W.params["decode_pos"]
+        self.cfg = hattn.preset("sliding")
+        ring = synth.cache_inputs(W.seed, 1, WINDOW, WINDOW, device, layer=0)
+        self.K0, self.V0 = ring["cache_k"], ring["cache_v"]   # positions P-512 .. P-1
+        self.K, self.V = self.K0.clone(), self.V0.clone()
+        ch = synth.layer_inputs(W.seed, 1, self.C, device, layer=1)
+        self.q, self.k_src, self.v, self.gate = ch["q"], ch["k"], ch["v"], ch["gate"]
+        self.k = torch.empty_like(self.k_src)
+        dc = synth.layer_inputs(W.seed, 1, 1, device, layer=2)
+        self.qd, self.kd_src, self.vd, self.gd = dc["q"], dc["k"], dc["v"], dc["gate"]
+        self.kd = torch.empty_like(self.kd_src)
+        self.pos0 = synth.positions(self.P, 1, device)
+        self.posd = synth.positions(self.pd, 1, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(1, self.C, HQ, dtype=torch.float32, device=device)
+        self.outd = torch.empty_like(self.qd)
+        self.lsed = torch.empty(1, 1, HQ, dtype=torch.float32, device=device)
+        self.ws = hattn.alloc_workspace(self.cfg, 1, WINDOW, device)
+        self.stages = Stages(["rope_k", "append", "prefill", "decode"])
+        self.prefill_flop = HQ * FLOP_PER_PAIR * prefill_pairs(self.C, self.P, "sliding")
+        self.decode_bytes = KV_BYTES_PER_TOKEN * WINDOW
+
+    def step(self):
+        h = self.h
+        self.K.copy_(self.K0)          # the ring as the previous chunk left it
+        self.V.copy_(self.V0)
+        self.k.copy_(self.k_src)
+        with self.stages.time("rope_k"):
+            h.rope_qk(self.cfg, None, self.k, self.pos0)
+        with self.stages.time("prefill"):
+            h.prefill_ring(self.cfg, self.q, self.k, self.v, self.K, self.V, self.pos0,
+                           self.gate, self.out, self.lse, rope_q_fused=True)
+        with self.stages.time("append"):
+            h.kv_append(self.cfg, self.k, self.v, self.K, self.V, self.pos0)
+        self.kd.copy_(self.kd_src)
+        with self.stages.time("rope_k"):
+            h.rope_qk(self.cfg, None, self.kd, self.posd)
+        with self.stages.time("append"):
+            h.kv_append(self.cfg, self.kd, self.vd, self.K, self.V, self.posd)
+        with self.stages.time("decode"):
+            h.decode(self.cfg, self.qd, self.K, self.V, self.posd, self.gd, self.outd, self.lsed,
+                     self.ws, rope_q_fused=True)
+
+
 def make_workload(idx: int, device="cuda"):
     if idx in (2, 3):
         return PrefillWorkload(idx, device)
@@ -228,6 +283,8 @@ def make_workload(idx: int, device="cuda"):
         return MixedDecodeWorkload(device)
     if idx == 5:
         return Full1MWorkload(device)
+    if idx == 6:
+        return SlidingRing1MWorkload(device)
     raise ValueError(f"no bench workload {idx} (1 is the parity-only tiny case)")
 
 
@@ -260,6 +317,23 @@ def cpu_baseline(wl, budget_s: float):
         return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                 "sample": f"prefill rows {done} of the 4096-query chunk over the full "
                           f"{wl.L0 + wl.C}-token cache, all 16 heads ({dt:.1f} s)"}
+    if isinstance(wl, SlidingRing1MWorkload):
+        rows = list(range(wl.C - 1, wl.C - 257, -1))
+        q, g = wl.q[0].cpu(), wl.gate[0].cpu()
+        _, kr = O.rope_qk(None, wl.k_src[0].cpu(), wl.P, "sliding")
+        v, K0, V0 = wl.v[0].cpu(), wl.K0[0].cpu(), wl.V0[0].cpu()
+        t0 = time.perf_counter()
+        done = []
+        for r in rows:
+            O.prefill_ring(q, kr, v, K0, V0, g, wl.P, rows=torch.tensor([r]))
+            done.append(r)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        flop = len(done) * HQ * FLOP_PER_PAIR * WINDOW
+        return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"{len(done)} prefill rows of the 4096-query chunk against the "
+                          f"ring, all 16 heads ({dt:.1f} s)"}
     if isinstance(wl, PrefillWorkload):
         b = 0
         S = wl.S
@@ -350,7 +424,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -393,7 +467,8 @@ def main():
         rec["prefill_TFLOPs_kernel"] = achieved
         rec["prefill_frac_mfma_peak"] = achieved / PEAK_BF16_TFLOPS
         tr_name = {5: "prefill_full_1m_chunk4096", 3: "prefill_full_b1_s131072",
-                   2: "prefill_sliding_b4_s32768"}[args.workload]
+                   2: "prefill_sliding_b4_s32768",
+                   6: "prefill_sliding_ring_1m_chunk4096"}[args.workload]
         rec["roofline"] = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,

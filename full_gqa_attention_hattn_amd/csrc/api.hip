@@ -152,6 +152,34 @@ hattn_status hattn_prefill(const hattn_layer_cfg* cfg, const void* q, const void
       scale_log2e(cfg), as_stream(stream)));
 }
 
+hattn_status hattn_prefill_ring(const hattn_layer_cfg* cfg, const void* q, const void* k_new,
+                                const void* v_new, const void* k_ring, const void* v_ring,
+                                const int32_t* pos0, int32_t B, int32_t Sq, const void* gate,
+                                void* out, float* lse, uint32_t flags, void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (cfg->kind != HATTN_SLIDING) return HATTN_ERR_UNSUPPORTED;
+  if (B < 0 || Sq < 0) return HATTN_ERR_SHAPE;
+  if ((flags & ~(uint32_t)HATTN_ROPE_Q_FUSED) != 0) return HATTN_ERR_UNSUPPORTED;
+  if ((long long)B * Sq == 0) return HATTN_OK;
+  if (!q || !k_new || !v_new || !k_ring || !v_ring || !pos0 || !gate || !out)
+    return HATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_ring) ||
+      !aligned16(v_ring) || !aligned16(out) || !aligned2(gate) || !aligned4(pos0) ||
+      (lse && !aligned4(lse)))
+    return HATTN_ERR_ALIGN;
+  const long long nqb = ((long long)Sq + 31) / 32;
+  const long long groups = (long long)B * hattn::kHkv * nqb + 8;
+  if (groups * 256 > kMaxWorkItems || (long long)B * Sq >= (1LL << 31)) return HATTN_ERR_SHAPE;
+  const hattn::RopeTable tab = rope_table(cfg);
+  return hip_status(hattn::launch_prefill_ring(
+      static_cast<const hattn::bf16_t*>(q), static_cast<const hattn::bf16_t*>(k_new),
+      static_cast<const hattn::bf16_t*>(v_new), static_cast<const hattn::bf16_t*>(k_ring),
+      static_cast<const hattn::bf16_t*>(v_ring), pos0, B, Sq,
+      static_cast<const hattn::bf16_t*>(gate), static_cast<hattn::bf16_t*>(out), lse,
+      cfg->window, (flags & HATTN_ROPE_Q_FUSED) != 0, tab, scale_log2e(cfg), as_stream(stream)));
+}
+
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
   if (check_cfg(cfg) != HATTN_OK || B < 0 || cap < 1) return 0;
   if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return 0;

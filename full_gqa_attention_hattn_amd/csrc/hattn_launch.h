@@ -22,6 +22,14 @@ hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* 
                           bf16_t* out, float* lse, int window, bool rope_q,
                           const RopeTable& tab, float scale_log2e, hipStream_t stream);
 
+// Sliding-layer chunk that continues a 512-slot ring: k_new / v_new [B, Sq, 4, 256] hold
+// the chunk's keys, k_ring / v_ring [B, 512, 4, 256] the older positions.
+hipError_t launch_prefill_ring(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
+                               const bf16_t* k_ring, const bf16_t* v_ring, const int* pos0, int B,
+                               int Sq, const bf16_t* gate, bf16_t* out, float* lse, int window,
+                               bool rope_q, const RopeTable& tab, float scale_log2e,
+                               hipStream_t stream);
+
 // Split-KV decode geometry, a pure function of (B, max keys per sequence).
 struct DecodePlan {
   int nchunks;  // key chunks per sequence

@@ -27,6 +27,13 @@
 //   * optional fused Q-RoPE: the workgroup computes cos/sin of its positions once into
 //     LDS and each lane rotates its own Q fragment (pairs d, d + r/2 sit in the same lane);
 //   * epilogue: 1/l, sigmoid gate, bf16 store, optional fp32 LSE.
+//
+// Ring mode (sliding layers only): a chunk at positions pos0.. continues a 512-slot ring
+// (slot = position mod 512).  Key positions stay absolute and tiles stay 32-aligned, so a
+// tile below pos0 is one contiguous run of ring slots, a tile at or past pos0 is a run of
+// the chunk's own rows, and only the tile that holds pos0 mixes the two, lane by lane.
+// [T2] "The real bottleneck of a million-token context" (sliding layers keep only the
+// most recent 512 tokens' keys and values).
 #include "hattn_device.h"
 #include "hattn_launch.h"
 
@@ -37,6 +44,7 @@ namespace {
 constexpr int kBN = 32;                  // keys per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleLog2 = 8.f;      // move the running max only when beaten by 2^8
+constexpr int kRingSlots = 512;          // sliding-layer ring: one slot per window position
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void g_void;
@@ -74,18 +82,42 @@ struct TileLoader {
     }
   }
 
-  // Rows at or past `cap` read row cap-1 instead; their scores are masked to -inf, so
-  // their values never reach the output.
-  __device__ __forceinline__ void load(char* dst, const bf16_t* base, int key0, int cap,
+  // Tile rows row0 .. row0 + 31 of `base`.  Rows past `last` (the last row any query of
+  // the workgroup can see) read row `last` instead: their scores are masked to -inf, and
+  // this way no row that the caller may not have written yet is ever read.
+  __device__ __forceinline__ void load(char* dst, const bf16_t* base, int row0, int last,
                                        int w) const {
-    const char* tile = reinterpret_cast<const char*>(base) + (long long)key0 * kRowBytes;
-    const bool tail = key0 + kBN > cap;
+    const char* tile = reinterpret_cast<const char*>(base) + (long long)row0 * kRowBytes;
+    const bool tail = row0 + kBN - 1 > last;
 #pragma unroll
     for (int i = 0; i < nw; ++i) {
-      const int r = tail ? min(lrow[i], cap - 1 - key0) : lrow[i];
+      const int r = tail ? min(lrow[i], last - row0) : lrow[i];
       const unsigned off = (unsigned)r * kRowBytes + (unsigned)lblk[i] * 16u;
       __builtin_amdgcn_global_load_lds((g_void*)(tile + off),
                                        (lds_void*)(dst + (nw * w + i) * 1024), 16, 0, 0);
+    }
+  }
+
+  // Ring mode, the one tile holding the chunk start: key positions key0 .. key0 + 31,
+  // those below pb from ring slot (position mod 512), the others from chunk row
+  // position - pb (at most 31, clamped to last_row).  Each lane issues the copy from its own
+  // source under a partial exec mask, so the tile can take up to twice the usual number
+  // of copy instructions; the caller then waits for all of them.
+  __device__ __forceinline__ void load_split(char* dst, const bf16_t* ring, const bf16_t* chunk,
+                                             int key0, int pb, int last_row, int w) const {
+    const char* rbase = reinterpret_cast<const char*>(ring);
+    const char* cbase = reinterpret_cast<const char*>(chunk);
+#pragma unroll
+    for (int i = 0; i < nw; ++i) {
+      const int j = key0 + lrow[i];
+      lds_void* d = (lds_void*)(dst + (nw * w + i) * 1024);
+      if (j < pb) {
+        const unsigned off = (unsigned)(j & (kRingSlots - 1)) * kRowBytes + (unsigned)lblk[i] * 16u;
+        __builtin_amdgcn_global_load_lds((g_void*)(rbase + off), d, 16, 0, 0);
+      } else {
+        const unsigned off = (unsigned)min(j - pb, last_row) * kRowBytes + (unsigned)lblk[i] * 16u;
+        __builtin_amdgcn_global_load_lds((g_void*)(cbase + off), d, 16, 0, 0);
+      }
     }
   }
 };
@@ -97,13 +129,17 @@ __device__ __forceinline__ void wait_lds_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
-template <bool kSliding, int kWaves, int kStages>
+// kc / vc: the position-indexed caches [B, cap, 4, 256], or in ring mode the chunk's own
+// keys / values [B, Sq, 4, 256] with the rings kr / vr [B, 512, 4, 256].
+template <bool kSliding, int kWaves, int kStages, bool kRing>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                    const bf16_t* __restrict__ vc, int cap, const int* __restrict__ pos0, int B,
+                    const bf16_t* __restrict__ vc, const bf16_t* __restrict__ kr,
+                    const bf16_t* __restrict__ vr, int cap, const int* __restrict__ pos0, int B,
                     int Sq, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
                     float* __restrict__ lse, int window, int rope_q, RopeTable tab, float sl2,
                     int nqb, int nwork) {
+  static_assert(kSliding || !kRing, "ring mode is for sliding layers");
   constexpr int kThreads = 64 * kWaves;
   constexpr int kRB = kWaves / kGroup;       // 32-row blocks per workgroup
   constexpr int kBQ = 32 * kRB;              // query positions per workgroup
@@ -145,7 +181,9 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int h = kvh * kGroup + (w % kGroup);
   const int i0 = qb * kBQ;
   const int nrows = min(kBQ, Sq - i0);
-  const int P0 = pos0[b] + i0;
+  // Clamped so that positions up to pb + Sq - 1 cannot overflow.
+  const int pb = min(pos0[b], 0x7fffffff - Sq);
+  const int P0 = pb + i0;
   const int Plast = P0 + nrows - 1;
   // This wave's rows: 32rb .. 32rb + 31 of the workgroup.
   const int r0 = 32 * rb;
@@ -155,17 +193,22 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int Pw0 = P0 + r0;                           // first row position of this wave
   const int Pwl = P0 + min(r0 + 31, nrows - 1);      // last valid row position of this wave
 
-  const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
+  // In ring mode every visible key exists (older ones in the ring, newer in the chunk).
+  const int capk = kRing ? Plast + 1 : cap;
+  const long long kv_off = ((long long)b * (kRing ? Sq : cap) * kHkv + kvh) * kD;
   const bf16_t* kbase = kc + kv_off;
   const bf16_t* vbase = vc + kv_off;
-  const int kmax = min(Plast, cap - 1);
+  const long long ring_off = kRing ? ((long long)b * kRingSlots * kHkv + kvh) * kD : 0;
+  const bf16_t* krbase = kr + ring_off;
+  const bf16_t* vrbase = vr + ring_off;
+  const int kmax = min(Plast, capk - 1);
   const int kmin = kSliding ? max(0, P0 - (window - 1)) : 0;
   const bool any_keys = kmax >= kmin;
   const int t_lo = any_keys ? kmin / kBN : 0;
   const int t_hi = any_keys ? kmax / kBN : -1;
   // Tiles this wave's rows can see at all (a workgroup's row blocks see different bands).
   const int wt_lo = kSliding ? max(0, Pw0 - (window - 1)) / kBN : 0;
-  const int wt_hi = min(Pwl, cap - 1) / kBN;
+  const int wt_hi = min(Pwl, capk - 1) / kBN;
 
   // Q^T operand: lane (n, hh) holds dims 16dc + 8hh .. +7 of query row n of this wave.
   bf16x8 qf[16];
@@ -223,6 +266,26 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
   const TileLoader<kWaves> ld(w, lane);
+  // K and V tile t (key positions 32t .. 32t + 31) into LDS stage st.
+  auto load_tile = [&](char* st, int t) {
+    const int key0 = t * kBN;
+    if (!kRing) {
+      ld.load(st, kbase, key0, kmax, w);
+      ld.load(st + kTile, vbase, key0, kmax, w);
+    } else if (key0 >= pb || key0 + kBN <= pb) {
+      // One source for the whole tile: a run of the chunk's rows, or of ring slots (tiles
+      // are 32-aligned, so a ring run does not wrap).  A single load() call for both keeps
+      // the per-lane offsets 32-bit and computed per tile.
+      const bool in_ring = key0 < pb;
+      const int row0 = in_ring ? (key0 & (kRingSlots - 1)) : key0 - pb;
+      const int last = in_ring ? row0 + kBN - 1 : kmax - pb;
+      ld.load(st, in_ring ? krbase : kbase, row0, last, w);
+      ld.load(st + kTile, in_ring ? vrbase : vbase, row0, last, w);
+    } else {
+      ld.load_split(st, krbase, kbase, key0, pb, kmax - pb, w);
+      ld.load_split(st + kTile, vrbase, vbase, key0, pb, kmax - pb, w);
+    }
+  };
   // The two waves sharing a SIMD (row blocks 0 and 1 of one head) would otherwise reach
   // their softmax phases together; issue priority for row block 0 staggers them.
   if (rb == 0) __builtin_amdgcn_s_setprio(2);
@@ -231,13 +294,11 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i) {
     const int t = t_lo + i;
-    if (t <= t_hi) {
-      char* st = smem + (i % kStages) * kStage;
-      ld.load(st, kbase, t * kBN, cap, w);
-      ld.load(st + kTile, vbase, t * kBN, cap, w);
-    }
+    if (t <= t_hi) load_tile(smem + (i % kStages) * kStage, t);
   }
-  if (t_lo + kStages - 2 <= t_hi) wait_lds_dma<kLoadsPerTile * (kStages - 2)>();
+  // (Ring mode: the tile holding the chunk start may issue more copies, so wait for all.)
+  constexpr int kAhead = kRing ? 0 : kLoadsPerTile * (kStages - 2);
+  if (t_lo + kStages - 2 <= t_hi) wait_lds_dma<kAhead>();
   else wait_lds_dma<0>();
   __syncthreads();
 
@@ -247,11 +308,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     const char* vst = kst + kTile;
     {
       const int tn = t + kStages - 1;  // refill the stage read during the previous tile
-      if (tn <= t_hi) {
-        char* st = smem + ((it + kStages - 1) % kStages) * kStage;
-        ld.load(st, kbase, tn * kBN, cap, w);
-        ld.load(st + kTile, vbase, tn * kBN, cap, w);
-      }
+      if (tn <= t_hi) load_tile(smem + ((it + kStages - 1) % kStages) * kStage, tn);
     }
 
     if (t >= wt_lo && t <= wt_hi) {
@@ -280,13 +337,13 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
       const int key0 = t * kBN;
-      const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= cap) &&
+      const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= capk) &&
                          (!kSliding || Pwl - key0 <= window - 1);
       if (!whole) {
 #pragma unroll
         for (int idx = 0; idx < 16; ++idx) {
           const int j = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
-          const bool vis = j <= prow && j < cap && (!kSliding || prow - j <= window - 1);
+          const bool vis = j <= prow && j < capk && (!kSliding || prow - j <= window - 1);
           s[idx] = vis ? s[idx] : -INFINITY;
         }
       }
@@ -354,7 +411,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     }
 
     // Tile t + 1 must have landed before the barrier; later tiles may stay in flight.
-    if (t + kStages - 1 <= t_hi) wait_lds_dma<kLoadsPerTile * (kStages - 2)>();
+    if (t + kStages - 1 <= t_hi) wait_lds_dma<kAhead>();
     else wait_lds_dma<0>();
     __syncthreads();
   }
@@ -389,19 +446,20 @@ constexpr int kWavesFull = 8;
 constexpr int kWavesSliding = 4;
 constexpr int kStagesSel = 2;  // K/V tiles resident in LDS
 
-template <bool kSliding, int kWaves>
-hipError_t launch_kind(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache, int cap,
-                       const int* pos0, int B, int Sq, const bf16_t* gate, bf16_t* out,
-                       float* lse, int window, bool rope_q, const RopeTable& tab,
-                       float scale_log2e, hipStream_t stream) {
+template <bool kSliding, int kWaves, bool kRing>
+hipError_t launch_kind(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+                       const bf16_t* k_ring, const bf16_t* v_ring, int cap, const int* pos0,
+                       int B, int Sq, const bf16_t* gate, bf16_t* out, float* lse, int window,
+                       bool rope_q, const RopeTable& tab, float scale_log2e, hipStream_t stream) {
   constexpr int kBQ = 32 * (kWaves / kGroup);
   const int nqb = (Sq + kBQ - 1) / kBQ;
   const long long nwork = (long long)B * kHkv * nqb;
   // Sliding grids are padded to a multiple of 8 for the XCD-contiguous mapping.
   const long long grid = kSliding ? (nwork + 7) / 8 * 8 : nwork;
-  hipLaunchKernelGGL((prefill_kernel<kSliding, kWaves, kStagesSel>), dim3((unsigned)grid),
-                     dim3(64 * kWaves), 0, stream, q, k_cache, v_cache, cap, pos0, B, Sq, gate,
-                     out, lse, window, rope_q ? 1 : 0, tab, scale_log2e, nqb, (int)nwork);
+  hipLaunchKernelGGL((prefill_kernel<kSliding, kWaves, kStagesSel, kRing>), dim3((unsigned)grid),
+                     dim3(64 * kWaves), 0, stream, q, k_cache, v_cache, k_ring, v_ring, cap, pos0,
+                     B, Sq, gate, out, lse, window, rope_q ? 1 : 0, tab, scale_log2e, nqb,
+                     (int)nwork);
   return hipGetLastError();
 }
 
@@ -412,10 +470,23 @@ hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* 
                           float* lse, int window, bool rope_q, const RopeTable& tab,
                           float scale_log2e, hipStream_t stream) {
   if (window > 0)
-    return launch_kind<true, kWavesSliding>(q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse,
-                                            window, rope_q, tab, scale_log2e, stream);
-  return launch_kind<false, kWavesFull>(q, k_cache, v_cache, cap, pos0, B, Sq, gate, out, lse,
-                                        window, rope_q, tab, scale_log2e, stream);
+    return launch_kind<true, kWavesSliding, false>(q, k_cache, v_cache, nullptr, nullptr, cap,
+                                                   pos0, B, Sq, gate, out, lse, window, rope_q,
+                                                   tab, scale_log2e, stream);
+  return launch_kind<false, kWavesFull, false>(q, k_cache, v_cache, nullptr, nullptr, cap, pos0, B,
+                                               Sq, gate, out, lse, window, rope_q, tab,
+                                               scale_log2e, stream);
+}
+
+hipError_t launch_prefill_ring(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
+                               const bf16_t* k_ring, const bf16_t* v_ring, const int* pos0, int B,
+                               int Sq, const bf16_t* gate, bf16_t* out, float* lse, int window,
+                               bool rope_q, const RopeTable& tab, float scale_log2e,
+                               hipStream_t stream) {
+  if (window != kRingSlots) return hipErrorInvalidValue;
+  return launch_kind<true, kWavesSliding, true>(q, k_new, v_new, k_ring, v_ring, Sq, pos0, B, Sq,
+                                                gate, out, lse, window, rope_q, tab, scale_log2e,
+                                                stream);
 }
 
 }  // namespace hattn

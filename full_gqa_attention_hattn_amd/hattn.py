@@ -28,6 +28,7 @@ HATTN_ROPE_Q_FUSED = 1
 
 # Every symbol include/hattn.h declares.
 EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_prefill",
+           "hattn_prefill_ring",
            "hattn_decode_workspace_bytes", "hattn_decode", "hattn_status_string",
            "hattn_last_hip_error")
 
@@ -63,6 +64,8 @@ def _load():
     lib.hattn_kv_append.restype = i32
     lib.hattn_prefill.argtypes = [cfgp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, u32, vp]
     lib.hattn_prefill.restype = i32
+    lib.hattn_prefill_ring.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, u32, vp]
+    lib.hattn_prefill_ring.restype = i32
     lib.hattn_decode_workspace_bytes.argtypes = [cfgp, i32, i32]
     lib.hattn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.hattn_decode.argtypes = [cfgp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
@@ -128,6 +131,18 @@ def prefill(cfg: LayerCfg, q, k_cache, v_cache, pos0, gate, out, lse=None,
     _check(_lib.hattn_prefill(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               int(k_cache.shape[1]), _ptr(pos0), B, Sq, _ptr(gate), _ptr(out),
                               _ptr(lse), flags, _stream(stream)), "hattn_prefill")
+
+
+def prefill_ring(cfg: LayerCfg, q, k_new, v_new, k_ring, v_ring, pos0, gate, out, lse=None,
+                 rope_q_fused: bool = True, stream=None):
+    """Sliding-layer chunk that continues the 512-slot rings k_ring / v_ring [B,512,4,256];
+    k_new / v_new [B,Sq,4,256] are the chunk's rotated keys and values."""
+    B, Sq = int(q.shape[0]), int(q.shape[1])
+    flags = HATTN_ROPE_Q_FUSED if rope_q_fused else 0
+    _check(_lib.hattn_prefill_ring(ctypes.byref(cfg), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_ring), _ptr(v_ring), _ptr(pos0), B, Sq, _ptr(gate),
+                                   _ptr(out), _ptr(lse), flags, _stream(stream)),
+           "hattn_prefill_ring")
 
 
 def decode_workspace_bytes(cfg: LayerCfg, B: int, cap: int) -> int:

@@ -129,6 +129,27 @@ hattn_status hattn_prefill(const hattn_layer_cfg* cfg, const void* q, const void
                            int32_t Sq, const void* gate, void* out, float* lse, uint32_t flags,
                            void* stream);
 
+/* Sliding-layer prefill of a chunk that continues a ring cache (cfg->kind must be
+ * HATTN_SLIDING, else HATTN_ERR_UNSUPPORTED).  Sequence b's chunk holds Sq tokens at
+ * positions p = pos0[b] + i, i < Sq:
+ *   q [B,Sq,16,256] (unrotated if flags & HATTN_ROPE_Q_FUSED, else rotated), gate [B,Sq,16];
+ *   k_new / v_new [B,Sq,4,256]: the chunk's rotated keys and values;
+ *   k_ring / v_ring [B,512,4,256]: the ring as hattn_kv_append leaves it after positions
+ *     0 .. pos0[b] - 1 were appended in order (slot = position mod 512).  Slots that no
+ *     position has reached yet (pos0[b] < 512) are never read.
+ * Query i sees positions max(0, p - 511) .. p: those below pos0[b] from the ring, the rest
+ * from k_new / v_new.  out [B,Sq,16,256] bf16, lse [B,Sq,16] fp32 or NULL; same arithmetic
+ * and empty-row rule as hattn_prefill.  The ring is only read: append the chunk with
+ * hattn_kv_append after this call (appending first would overwrite keys that the chunk's
+ * earlier rows still see).  pos0[b] >= 0 and pos0[b] + Sq <= 2^31 - 1; the kernel clamps
+ * larger positions and never reads outside the given buffers.
+ * [T2] "The real bottleneck of a million-token context" (sliding layers keep only the last
+ * 512 tokens' keys and values); [T3] "Sliding window 512"; [T1] "Hybrid attention". */
+hattn_status hattn_prefill_ring(const hattn_layer_cfg* cfg, const void* q, const void* k_new,
+                                const void* v_new, const void* k_ring, const void* v_ring,
+                                const int32_t* pos0, int32_t B, int32_t Sq, const void* gate,
+                                void* out, float* lse, uint32_t flags, void* stream);
+
 /* Bytes of device workspace hattn_decode needs for B sequences and this cache capacity
  * (its split-KV partial results).  0 for an invalid configuration. */
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap);

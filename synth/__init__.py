@@ -119,6 +119,12 @@ WORKLOADS = {
                 "1M-context full layer, B=1: cache of positions 0..1044479, chunked "
                 "prefill of 4096 queries at 1044480..1048575, then one decode at 1048576",
                 1239, dict(B=1, cache_len=1044480, chunk=4096, decode_pos=1 << 20)),
+    6: Workload(6, "sliding_ring_1m_chunk4096_decode",
+                "1M-context sliding layer, B=1: 512-slot ring holding positions "
+                "1043968..1044479, chunk prefill of 4096 queries at 1044480..1048575 "
+                "against the ring, the chunk appended, then one ring decode at 1048576",
+                1240, dict(B=1, ring_pos=1044480, chunk=4096, decode_pos=1 << 20,
+                           window=512)),
 }
 
 

@@ -50,7 +50,8 @@ def assert_rel_l2(gpu, ref, name, tol=REL_L2_TOL):
     den = r.norm(dim=-1).clamp_min(1e-30)
     rel = num / den
     worst = float(rel.max())
-    assert worst <= tol, f"{name}: worst per-row relative L2 error {worst:.3e}"
+    at = [int(i) for i in torch.nonzero(rel == rel.max())[0]]
+    assert worst <= tol, f"{name}: worst per-row relative L2 error {worst:.3e} at index {at}"
     return worst
 
 
@@ -59,3 +60,17 @@ def check_outputs(gpu_out, gpu_lse, ref_out, ref_lse, name):
     e2 = assert_rel_l2(gpu_out, ref_out, name)
     e3 = assert_lse_close(gpu_lse, ref_lse, name) if gpu_lse is not None else None
     say(f"{name}: max abs err {e1:.2e}, worst rel-L2 {e2:.2e}, LSE err {e3}")
+
+
+def check_needle_row(gpu_out, gpu_lse, ref_out, ref_lse, name):
+    """A planted-needle row: element tolerance as usual; its LSE, set by a logit of ~32
+    or by logits spread far wider than N(0, 1), is held to 1e-2 + 2^-7 |LSE|.  The bf16
+    operands of a needle (amplitude 16 on two rotated dims) carry a rounding error that
+    scales the row's logits by a common 1 + O(2^-9) each, which moves the LSE in
+    proportion to its size; a leaked or missed needle moves it by ~25."""
+    e1 = assert_bf16_close(gpu_out, ref_out, name)
+    g = gpu_lse.detach().to("cpu", torch.float64)
+    r = ref_lse.detach().to("cpu", torch.float64)
+    err = (g - r).abs()
+    assert bool((err <= 1e-2 + 2 ** -7 * r.abs()).all()), f"{name}: LSE err {float(err.max()):.3e}"
+    say(f"{name}: max abs err {e1:.2e}, LSE err {float(err.max()):.2e}")

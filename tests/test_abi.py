@@ -132,6 +132,33 @@ def test_prefill_validation(h):
     assert lib.hattn_prefill(c, *args(B=65536, S=1 << 15), None) == h.HATTN_ERR_SHAPE
 
 
+def test_prefill_ring_validation(h):
+    lib = h.lib()
+    s, f = _cfg(h, "sliding"), _cfg(h, "full")
+    names = ("q", "kn", "vn", "kr", "vr", "pos", "B", "S", "g", "out", "lse", "flags")
+    base = dict(q=A, kn=A, vn=A, kr=A, vr=A, pos=A, B=2, S=40, g=A, out=A, lse=None, flags=0)
+
+    def call(cfg=s, **o):
+        a = dict(base, **o)
+        return lib.hattn_prefill_ring(cfg, *[a[k] for k in names], None)
+
+    assert call(cfg=f) == h.HATTN_ERR_UNSUPPORTED         # ring continuation is sliding-only
+    assert call(cfg=None) == h.HATTN_ERR_NULL
+    for k in ("q", "kn", "vn", "kr", "vr", "pos", "g", "out"):
+        assert call(**{k: None}) == h.HATTN_ERR_NULL, k
+        if k not in ("pos", "g"):
+            assert call(**{k: MIS}) == h.HATTN_ERR_ALIGN, k
+    assert call(g=P(0x10001)) == h.HATTN_ERR_ALIGN
+    assert call(pos=P(0x10002)) == h.HATTN_ERR_ALIGN
+    assert call(lse=P(0x10002)) == h.HATTN_ERR_ALIGN
+    assert call(S=-1) == h.HATTN_ERR_SHAPE
+    assert call(B=-1) == h.HATTN_ERR_SHAPE
+    assert call(flags=2) == h.HATTN_ERR_UNSUPPORTED
+    assert call(B=65536, S=1 << 15) == h.HATTN_ERR_SHAPE
+    assert call(S=0, q=None, kn=None) == h.HATTN_OK     # empty: no launch, pointers unread
+    assert call(B=0) == h.HATTN_OK
+
+
 def test_decode_validation_and_workspace(h):
     lib = h.lib()
     f, s = _cfg(h, "full"), _cfg(h, "sliding")

@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import synth
-from parity import check_outputs, say
+from parity import check_needle_row, check_outputs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -158,4 +158,46 @@ def test_full_1m_chunk_and_decode(bench):
     torch.cuda.synchronize()
     assert float((od[0, 0].float() - wl.out[0, row].float()).abs().max()) < 1e-2
     assert float((lsed[0, 0] - wl.lse[0, row]).abs().max()) < 1e-3
+    _free(wl)
+
+
+def test_sliding_ring_1m_chunk_and_decode(bench):
+    say("workload 6: 1M sliding layer, chunk against the ring + decode")
+    wl = bench.make_workload(6)
+    # needles among the chunk's own keys: visible at distance 511, invisible at 512
+    synth.plant_needle(wl.q, wl.k_src, 0, 1500, 1500 - 511, (127, 255), 16.0)
+    synth.plant_needle(wl.q, wl.k_src, 0, 2500, 2500 - 512, (127, 255), 16.0)
+    wl.step()
+    torch.cuda.synchronize()
+    P = wl.P
+    _, kr = O.rope_qk(None, _cpu(wl.k_src[0]), P, "sliding")
+    gen = torch.Generator().manual_seed(8)
+    rows = sorted(set(list(range(0, 40)) + list(range(495, 530))
+                      + list(range(wl.C - 20, wl.C))
+                      + torch.randint(0, wl.C, (24,), generator=gen).tolist()) - {1500, 2500})
+    rows_t = torch.tensor(rows)
+    y, l = O.prefill_ring(_cpu(wl.q[0]), kr, _cpu(wl.v[0]), _cpu(wl.K0[0]), _cpu(wl.V0[0]),
+                          _cpu(wl.gate[0]), P, rows=rows_t)
+    check_outputs(_cpu(wl.out[0])[rows_t], _cpu(wl.lse[0])[rows_t], y, l,
+                  f"w6 prefill ({len(rows)} rows)")
+    for r in (1500, 2500):
+        yn, ln = O.prefill_ring(_cpu(wl.q[0]), kr, _cpu(wl.v[0]), _cpu(wl.K0[0]), _cpu(wl.V0[0]),
+                                _cpu(wl.gate[0]), P, rows=torch.tensor([r]))
+        check_needle_row(_cpu(wl.out[0, r]), _cpu(wl.lse[0, r]), yn[0], ln[0], f"w6 needle row {r}")
+    tgt = _needle_target(wl.v[0, 1500 - 511], wl.gate[0, 1500])
+    for hq in range(16):
+        got = _cpu(wl.out[0, 1500, hq]).double()
+        assert float((got - tgt[hq]).norm() / tgt[hq].norm()) < 2e-2
+    tgt = _needle_target(wl.v[0, 2500 - 512], wl.gate[0, 2500])
+    for hq in range(16):
+        got = _cpu(wl.out[0, 2500, hq]).double()
+        assert float((got - tgt[hq]).norm() / tgt[hq].norm()) > 0.5
+    # decode at 2^20 over the ring after the chunk and the new token were appended
+    ring_k = _cpu(wl.K0[0]).float()
+    ring_v = _cpu(wl.V0[0]).float()
+    O.kv_append(ring_k, ring_v, kr, _cpu(wl.v[0]).float(), P, "sliding")
+    _, kd = O.rope_qk(None, _cpu(wl.kd_src[0]), wl.pd, "sliding")
+    O.kv_append(ring_k, ring_v, kd, _cpu(wl.vd[0]).float(), wl.pd, "sliding")
+    yd, ld = O.decode(_cpu(wl.qd[0, 0]), ring_k, ring_v, _cpu(wl.gd[0, 0]), wl.pd, "sliding")
+    check_outputs(_cpu(wl.outd[0, 0]), _cpu(wl.lsed[0, 0]), yd, ld, "w6 ring decode p=2^20")
     _free(wl)
