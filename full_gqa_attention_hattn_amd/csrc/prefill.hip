@@ -384,7 +384,8 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
         pf[c] = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
       }
       // V^T fragment i = 8c + mb: keys 16c + trow (slots 0..3) and 16c + 8 + trow (slots
-      // 4..7), dims 32mb + 16(g&1) + ..; read one MFMA ahead of its use.
+      // 4..7), dims 32mb + 16(g&1) + ..; read three MFMAs ahead of its use (measured: the
+      // transposing reads need more cover than the K reads, which run two ahead).
       auto vfrag = [&](int i) {
         const int c = i >> 3, mb = i & 7;
         const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
@@ -394,20 +395,26 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
         return __builtin_bit_cast(bf16x8,
                                   s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
       };
-      bf16x8 va = vfrag(0);
+      constexpr int kVAhead = 3;
+      bf16x8 vq[kVAhead];
+#pragma unroll
+      for (int a = 0; a < kVAhead; ++a) vq[a] = vfrag(a);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bf16x8 vn = i + 1 < 16 ? vfrag(i + 1) : va;
-        o[i & 7] = mfma32(va, pf[i >> 3], o[i & 7]);
-        va = vn;
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        const bf16x8 vn = i + kVAhead < 16 ? vfrag(i + kVAhead) : vq[0];
+        o[i & 7] = mfma32(vq[0], pf[i >> 3], o[i & 7]);
 #pragma unroll
-      for (int i = 0; i < 14; ++i) {
+        for (int a = 0; a + 1 < kVAhead; ++a) vq[a] = vq[a + 1];
+        vq[kVAhead - 1] = vn;
+      }
+      // Two transposing reads per fragment: 2 * kVAhead up front, then two per MFMA.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
+#pragma unroll
+      for (int i = 0; i < 16 - kVAhead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 1);
     }
 
     // Tile t + 1 must have landed before the barrier; later tiles may stay in flight.
