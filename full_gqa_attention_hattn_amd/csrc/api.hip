@@ -79,6 +79,8 @@ int decode_max_keys(const hattn_layer_cfg* cfg, int32_t cap) {
 
 }  // namespace
 
+int32_t hattn::note_hip_error(hipError_t e) { return hip_status(e == hipSuccess ? hipErrorUnknown : e); }
+
 extern "C" {
 
 hattn_status hattn_cfg_preset(int32_t kind, hattn_layer_cfg* out) {
@@ -105,9 +107,13 @@ hattn_status hattn_rope_qk(const hattn_layer_cfg* cfg, void* q, void* k, const i
                                           as_stream(stream)));
 }
 
-hattn_status hattn_kv_append(const hattn_layer_cfg* cfg, const void* k_new, const void* v_new,
-                             void* k_cache, void* v_cache, int32_t cap, const int32_t* pos0,
-                             int32_t B, int32_t n, int32_t* slots_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+hattn_status kv_append_impl(const hattn_layer_cfg* cfg, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, int32_t cap, const int32_t* pos0,
+                            int32_t B, int32_t n, int32_t* slots_out, bool rope, void* stream) {
   hattn_status st = check_cfg(cfg);
   if (st != HATTN_OK) return st;
   if (B < 0 || n < 0 || cap < 1) return HATTN_ERR_SHAPE;
@@ -119,10 +125,31 @@ hattn_status hattn_kv_append(const hattn_layer_cfg* cfg, const void* k_new, cons
       !aligned4(pos0) || (slots_out && !aligned4(slots_out)))
     return HATTN_ERR_ALIGN;
   if (ntok * 256 > kMaxWorkItems) return HATTN_ERR_SHAPE;
+  const hattn::RopeTable tab = rope_table(cfg);
   return hip_status(hattn::launch_kv_append(
       static_cast<const hattn::bf16_t*>(k_new), static_cast<const hattn::bf16_t*>(v_new),
       static_cast<hattn::bf16_t*>(k_cache), static_cast<hattn::bf16_t*>(v_cache), cap, pos0, B, n,
-      cfg->kind == HATTN_SLIDING ? cfg->window : 0, slots_out, as_stream(stream)));
+      cfg->kind == HATTN_SLIDING ? cfg->window : 0, slots_out, rope ? &tab : nullptr,
+      as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+hattn_status hattn_kv_append(const hattn_layer_cfg* cfg, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, int32_t cap, const int32_t* pos0,
+                             int32_t B, int32_t n, int32_t* slots_out, void* stream) {
+  return kv_append_impl(cfg, k_new, v_new, k_cache, v_cache, cap, pos0, B, n, slots_out, false,
+                        stream);
+}
+
+hattn_status hattn_kv_append_rope(const hattn_layer_cfg* cfg, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache, int32_t cap,
+                                  const int32_t* pos0, int32_t B, int32_t n, int32_t* slots_out,
+                                  void* stream) {
+  return kv_append_impl(cfg, k_new, v_new, k_cache, v_cache, cap, pos0, B, n, slots_out, true,
+                        stream);
 }
 
 hattn_status hattn_prefill(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         float sv, cv;
         sincos_angle(rope_angle(p, tab.inv_freq[32 * dc + 8 * g + e]), &sv, &cv);
         const float a = (float)xa[e], bb = (float)xb[e];
-        const float ya = a * cv - bb * sv, yb = bb * cv + a * sv;
+        float ya, yb;
+        rope_pair(a, bb, cv, sv, &ya, &yb);
         if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
       }
       const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);

@@ -91,6 +91,17 @@ __device__ __forceinline__ float rope_angle(int p, float inv_freq) {
   return __fmul_rn((float)p, inv_freq);
 }
 
+// One rotate-half pair (x_i, x_{i+r/2}) turned by the angle whose cosine and sine are
+// (c, s):  y_i = x_i c - x_{i+r/2} s,  y_{i+r/2} = x_{i+r/2} c + x_i s.  The product with s
+// is rounded first and the one with c fused into it, written out so that every kernel
+// that rotates (standalone RoPE, the rotating append, the fused Q prologues) produces the
+// same bits.
+__device__ __forceinline__ void rope_pair(float a, float b, float c, float s, float* ya,
+                                          float* yb) {
+  *ya = __builtin_fmaf(a, c, -__fmul_rn(b, s));
+  *yb = __builtin_fmaf(b, c, __fmul_rn(a, s));
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 }  // namespace hattn

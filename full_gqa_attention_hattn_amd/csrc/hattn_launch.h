@@ -9,12 +9,18 @@
 
 namespace hattn {
 
+// Record e as the calling thread's last HIP error and return HATTN_ERR_HIP (api.hip).
+int32_t note_hip_error(hipError_t e);
+
 hipError_t launch_rope_qk(bf16_t* q, bf16_t* k, const int* pos0, int B, int S,
                           const RopeTable& tab, hipStream_t stream);
 
+// rope_k: NULL copies k_new as given; otherwise each key is rotated by its position with
+// this table while it is copied (k_new itself is not modified).
 hipError_t launch_kv_append(const bf16_t* k_new, const bf16_t* v_new, bf16_t* k_cache,
                             bf16_t* v_cache, int cap, const int* pos0, int B, int n,
-                            int window, int* slots_out, hipStream_t stream);
+                            int window, int* slots_out, const RopeTable* rope_k,
+                            hipStream_t stream);
 
 // window == 0 selects the full-causal kernel.
 hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,

@@ -238,8 +238,8 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       for (int e = 0; e < 8; ++e) {
         const f32x2 c = c8[e];
         const float a = (float)xa[e], bb = (float)xb[e];
-        const float ya = a * c.x - bb * c.y;
-        const float yb = bb * c.x + a * c.y;
+        float ya, yb;
+        rope_pair(a, bb, c.x, c.y, &ya, &yb);
         if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
       }
       const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);

@@ -68,9 +68,11 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(
       const f32x2 c0 = cs[t][d0 + 2 * w], c1 = cs[t][d0 + 2 * w + 1];
       const float a0 = bf16_lo(wa[w]), a1 = bf16_hi(wa[w]);
       const float b0 = bf16_lo(wb[w]), b1 = bf16_hi(wb[w]);
-      // y_i = x_i c - x_{i+r/2} s ;  y_{i+r/2} = x_{i+r/2} c + x_i s
-      ya[w] = pack_bf16x2(a0 * c0.x - b0 * c0.y, a1 * c1.x - b1 * c1.y);
-      yb[w] = pack_bf16x2(b0 * c0.x + a0 * c0.y, b1 * c1.x + a1 * c1.y);
+      float ya0, yb0, ya1, yb1;
+      rope_pair(a0, b0, c0.x, c0.y, &ya0, &yb0);
+      rope_pair(a1, b1, c1.x, c1.y, &ya1, &yb1);
+      ya[w] = pack_bf16x2(ya0, ya1);
+      yb[w] = pack_bf16x2(yb0, yb1);
     }
     *reinterpret_cast<uint4*>(row + d0) = uint4{ya[0], ya[1], ya[2], ya[3]};
     *reinterpret_cast<uint4*>(row + d0 + half) = uint4{yb[0], yb[1], yb[2], yb[3]};
@@ -78,11 +80,16 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(
 }
 
 // One workgroup per appended token: threads 0..127 copy its key row (4 heads x 256 dims),
-// threads 128..255 its value row, 16 bytes each.
+// threads 128..255 its value row, 16 bytes each.  With rope_k the key is rotated by its
+// position on the way (same arithmetic as rope_qk_kernel): the thread holding dims
+// d .. d+7 < r/2 of a head also reads and writes their partners d + r/2 .., the threads
+// of dims r/2 .. r-1 write nothing, and dims r .. 255 are copied.
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
     bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache, int cap,
-    const int* __restrict__ pos0, int n, int window, int* __restrict__ slots_out) {
+    const int* __restrict__ pos0, int n, int window, int* __restrict__ slots_out, int rope_k,
+    RopeTable tab) {
+  __shared__ f32x2 cs[kMaxHalfRot];
   const long long tok = blockIdx.x;
   const int b = (int)(tok / n), t = (int)(tok - (long long)b * n);
   const int p = pos0[b] + t;
@@ -98,12 +105,42 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     write = slot >= 0 && slot < cap && t >= n - window;
   }
   if (threadIdx.x == 0 && slots_out != nullptr) slots_out[tok] = slot;
-  if (!write) return;
+  if (!write) return;  // uniform over the workgroup
+  const int half = tab.rot_dim >> 1;
+  if (rope_k) {
+    for (int f = threadIdx.x; f < half; f += 256) {
+      float sv, cv;
+      sincos_angle(rope_angle(p, tab.inv_freq[f]), &sv, &cv);
+      cs[f] = f32x2{cv, sv};
+    }
+    __syncthreads();
+  }
   const int c = threadIdx.x & 127;
   const bool is_v = threadIdx.x >= 128;
   const bf16_t* src = (is_v ? v_new : k_new) + tok * (kHkv * kD) + c * 8;
   bf16_t* dst = (is_v ? v_cache : k_cache) + ((long long)b * cap + slot) * (kHkv * kD) + c * 8;
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  const int d0 = (c & 31) * 8;  // first of this thread's 8 dims within its head
+  if (!rope_k || is_v || d0 >= 2 * half) {
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    return;
+  }
+  if (d0 >= half) return;  // the partner thread writes these dims
+  const uint4 xa = *reinterpret_cast<const uint4*>(src);
+  const uint4 xb = *reinterpret_cast<const uint4*>(src + half);
+  const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
+  const uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
+  uint32_t ya[4], yb[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 c0 = cs[d0 + 2 * w], c1 = cs[d0 + 2 * w + 1];
+    float ya0, yb0, ya1, yb1;
+    rope_pair(bf16_lo(wa[w]), bf16_lo(wb[w]), c0.x, c0.y, &ya0, &yb0);
+    rope_pair(bf16_hi(wa[w]), bf16_hi(wb[w]), c1.x, c1.y, &ya1, &yb1);
+    ya[w] = pack_bf16x2(ya0, ya1);
+    yb[w] = pack_bf16x2(yb0, yb1);
+  }
+  *reinterpret_cast<uint4*>(dst) = uint4{ya[0], ya[1], ya[2], ya[3]};
+  *reinterpret_cast<uint4*>(dst + half) = uint4{yb[0], yb[1], yb[2], yb[3]};
 }
 
 }  // namespace
@@ -119,10 +156,12 @@ hipError_t launch_rope_qk(bf16_t* q, bf16_t* k, const int* pos0, int B, int S,
 
 hipError_t launch_kv_append(const bf16_t* k_new, const bf16_t* v_new, bf16_t* k_cache,
                             bf16_t* v_cache, int cap, const int* pos0, int B, int n,
-                            int window, int* slots_out, hipStream_t stream) {
+                            int window, int* slots_out, const RopeTable* rope_k,
+                            hipStream_t stream) {
   const long long grid = (long long)B * n;
+  const RopeTable tab = rope_k ? *rope_k : RopeTable{};
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new,
-                     k_cache, v_cache, cap, pos0, n, window, slots_out);
+                     k_cache, v_cache, cap, pos0, n, window, slots_out, rope_k ? 1 : 0, tab);
   return hipGetLastError();
 }
 

@@ -27,10 +27,12 @@ HATTN_FULL = 1
 HATTN_ROPE_Q_FUSED = 1
 
 # Every symbol include/hattn.h declares.
-EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_prefill",
-           "hattn_prefill_ring",
-           "hattn_decode_workspace_bytes", "hattn_decode", "hattn_status_string",
-           "hattn_last_hip_error")
+EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_kv_append_rope",
+           "hattn_prefill", "hattn_prefill_ring",
+           "hattn_decode_workspace_bytes", "hattn_decode", "hattn_model_layer_kind",
+           "hattn_model_kv_bytes", "hattn_model_decode_workspace_bytes", "hattn_model_decode",
+           "hattn_model_prefill_workspace_bytes", "hattn_model_prefill",
+           "hattn_status_string", "hattn_last_hip_error")
 
 
 class LayerCfg(ctypes.Structure):
@@ -39,6 +41,12 @@ class LayerCfg(ctypes.Structure):
                 ("window", ctypes.c_int32), ("rot_dim", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
                 ("reserved", ctypes.c_int32)]
+
+
+class LayerIO(ctypes.Structure):
+    """hattn_layer_io: one layer's device buffers for the whole-model driver."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "k", "v", "gate", "k_cache", "v_cache", "out", "lse")]
 
 
 class HattnError(RuntimeError):
@@ -62,6 +70,22 @@ def _load():
     lib.hattn_rope_qk.restype = i32
     lib.hattn_kv_append.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
     lib.hattn_kv_append.restype = i32
+    lib.hattn_kv_append_rope.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
+    lib.hattn_kv_append_rope.restype = i32
+    iop = ctypes.POINTER(LayerIO)
+    sz = ctypes.c_size_t
+    lib.hattn_model_layer_kind.argtypes = [i32]
+    lib.hattn_model_layer_kind.restype = i32
+    lib.hattn_model_kv_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.hattn_model_kv_bytes.restype = i32
+    lib.hattn_model_decode_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.hattn_model_decode_workspace_bytes.restype = sz
+    lib.hattn_model_decode.argtypes = [iop, i32, i32, vp, i32, vp, sz, vp]
+    lib.hattn_model_decode.restype = i32
+    lib.hattn_model_prefill_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.hattn_model_prefill_workspace_bytes.restype = sz
+    lib.hattn_model_prefill.argtypes = [iop, i32, i32, vp, i32, i32, vp, sz, vp]
+    lib.hattn_model_prefill.restype = i32
     lib.hattn_prefill.argtypes = [cfgp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, u32, vp]
     lib.hattn_prefill.restype = i32
     lib.hattn_prefill_ring.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, u32, vp]
@@ -124,6 +148,15 @@ def kv_append(cfg: LayerCfg, k_new, v_new, k_cache, v_cache, pos0, slots_out=Non
                                 _ptr(slots_out), _stream(stream)), "hattn_kv_append")
 
 
+def kv_append_rope(cfg: LayerCfg, k_new, v_new, k_cache, v_cache, pos0, slots_out=None,
+                   stream=None):
+    """kv_append with unrotated k_new, rotated by position on the way into the cache."""
+    B, n = int(k_new.shape[0]), int(k_new.shape[1])
+    _check(_lib.hattn_kv_append_rope(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                     _ptr(v_cache), int(k_cache.shape[1]), _ptr(pos0), B, n,
+                                     _ptr(slots_out), _stream(stream)), "hattn_kv_append_rope")
+
+
 def prefill(cfg: LayerCfg, q, k_cache, v_cache, pos0, gate, out, lse=None,
             rope_q_fused: bool = True, stream=None):
     B, Sq = int(q.shape[0]), int(q.shape[1])
@@ -163,3 +196,52 @@ def decode(cfg: LayerCfg, q, k_cache, v_cache, pos, gate, out, lse=None, workspa
 def alloc_workspace(cfg: LayerCfg, B: int, cap: int, device="cuda"):
     n = decode_workspace_bytes(cfg, B, cap)
     return torch.empty(max(16, n), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ whole-model driver --
+def model_layer_kind(layer: int) -> str:
+    return "full" if _lib.hattn_model_layer_kind(int(layer)) == HATTN_FULL else "sliding"
+
+
+def model_kv_bytes(n_layers: int, B: int, cap: int):
+    """(per-layer KV bytes, total) of the layer schedule."""
+    per = (ctypes.c_size_t * n_layers)()
+    tot = ctypes.c_size_t(0)
+    _check(_lib.hattn_model_kv_bytes(n_layers, B, cap, per, ctypes.byref(tot)),
+           "hattn_model_kv_bytes")
+    return list(per), int(tot.value)
+
+
+def _layer_array(layers):
+    arr = (LayerIO * len(layers))()
+    for i, L in enumerate(layers):
+        for name in ("q", "k", "v", "gate", "k_cache", "v_cache", "out", "lse"):
+            t = L.get(name)
+            setattr(arr[i], name, None if t is None else t.data_ptr())
+    return arr
+
+
+def model_decode_workspace_bytes(n_layers: int, B: int, cap: int) -> int:
+    return int(_lib.hattn_model_decode_workspace_bytes(n_layers, B, cap))
+
+
+def model_prefill_workspace_bytes(n_layers: int, B: int, Sq: int) -> int:
+    return int(_lib.hattn_model_prefill_workspace_bytes(n_layers, B, Sq))
+
+
+def model_decode(layers, cap: int, pos, workspace, stream=None):
+    """One decode step of every layer; layers: list of dicts with the LayerIO fields."""
+    arr = _layer_array(layers)
+    B = int(layers[0]["q"].shape[0])
+    _check(_lib.hattn_model_decode(arr, len(layers), cap, _ptr(pos), B, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "hattn_model_decode")
+
+
+def model_prefill(layers, cap: int, pos0, workspace, stream=None):
+    """One prefill chunk through every layer (chunks in position order)."""
+    arr = _layer_array(layers)
+    B, Sq = int(layers[0]["q"].shape[0]), int(layers[0]["q"].shape[1])
+    _check(_lib.hattn_model_prefill(arr, len(layers), cap, _ptr(pos0), B, Sq, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "hattn_model_prefill")

@@ -110,6 +110,17 @@ hattn_status hattn_kv_append(const hattn_layer_cfg* cfg, const void* k_new, cons
                              void* k_cache, void* v_cache, int32_t cap, const int32_t* pos0,
                              int32_t B, int32_t n, int32_t* slots_out, void* stream);
 
+/* hattn_kv_append with the RoPE of the keys fused in: k_new [B,n,4,256] holds UNROTATED
+ * keys, and each is rotated by its position (the arithmetic of hattn_rope_qk, bit for bit)
+ * as it is written to the cache; k_new itself is not modified, so a captured sequence of
+ * calls can be replayed.  Slots, ring rules, status codes and v_new as in hattn_kv_append.
+ * [T1] "Per-layer RoPE and the local/global split"; [T2] "The real bottleneck of a
+ * million-token context". */
+hattn_status hattn_kv_append_rope(const hattn_layer_cfg* cfg, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache, int32_t cap,
+                                  const int32_t* pos0, int32_t B, int32_t n, int32_t* slots_out,
+                                  void* stream);
+
 /* Prefill attention for Sq query tokens per sequence.
  *   q [B,Sq,16,256] (unrotated if flags & HATTN_ROPE_Q_FUSED, else rotated);
  *   k_cache / v_cache [B,cap,4,256]: rotated keys and values indexed by absolute position
@@ -170,6 +181,64 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
                           const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
                           const void* gate, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* ---- Whole-model driver ------------------------------------------------------------
+ * The model's layers follow one schedule: layer l is full-causal iff l % 4 == 3, every
+ * other layer sliding-window (36 layers: 9 full, 27 sliding).  [T1] "Hybrid attention:
+ * only one layer in four gets the full view"; [T2] "27 sliding-window layers plus 9 global
+ * layers"; [T3] "36-layer hybrid layout". */
+
+/* HATTN_FULL or HATTN_SLIDING for layer index `layer` (-1 if negative). */
+int32_t hattn_model_layer_kind(int32_t layer);
+
+/* KV-cache bytes of the schedule for B sequences: a full layer keeps cap tokens, a sliding
+ * layer its 512-slot ring, each token 4096 bytes (K and V, 4 heads x 256 dims x bf16).
+ * per_layer (host, n_layers entries) may be NULL; total (host) is required.
+ * HATTN_ERR_SHAPE unless 1 <= n_layers <= 4096, B >= 0, cap >= 512.
+ * [T1] "Doing the arithmetic first" (4096 bytes per token per layer). */
+hattn_status hattn_model_kv_bytes(int32_t n_layers, int32_t B, int32_t cap, size_t* per_layer,
+                                  size_t* total);
+
+/* One layer's buffers for a driver call (all device memory, layouts as above):
+ *   q [B,S,16,256], k / v [B,S,4,256] (q and k UNROTATED), gate [B,S,16];
+ *   k_cache / v_cache: full layers [B,cap,4,256] (position-indexed), sliding layers the
+ *     ring [B,512,4,256];  out [B,S,16,256];  lse [B,S,16] fp32 or NULL.
+ * S is 1 for hattn_model_decode and Sq for hattn_model_prefill.  Inputs are only read. */
+typedef struct hattn_layer_io {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gate;
+  void* k_cache;
+  void* v_cache;
+  void* out;
+  float* lse;
+} hattn_layer_io;
+
+/* Device workspace hattn_model_decode needs (0 for invalid sizes). */
+size_t hattn_model_decode_workspace_bytes(int32_t n_layers, int32_t B, int32_t cap);
+
+/* One decode step of every layer, in layer order, on `stream`: for each layer the new
+ * token at pos[b] (int32 [B], device) is rotated and appended (hattn_kv_append_rope) and
+ * attended (hattn_decode with HATTN_ROPE_Q_FUSED).  layers: host array of n_layers.
+ * Nothing is allocated and no input is modified, so a captured step replays exactly.
+ * All pointers are checked before anything is enqueued; a later non-OK status can only
+ * be HATTN_ERR_HIP.  Errors: those of the per-layer calls, HATTN_ERR_WORKSPACE. */
+hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, int32_t cap,
+                                const int32_t* pos, int32_t B, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Device workspace hattn_model_prefill needs: one sliding layer's rotated chunk keys. */
+size_t hattn_model_prefill_workspace_bytes(int32_t n_layers, int32_t B, int32_t Sq);
+
+/* One prefill chunk of Sq tokens per sequence (positions pos0[b] ..) through every layer:
+ *   full:    hattn_kv_append_rope into the cache, then hattn_prefill over it;
+ *   sliding: the chunk's keys are rotated into the workspace, attended together with the
+ *            ring (hattn_prefill_ring), then appended to the ring.
+ * Chunks must arrive in position order, each after the previous one's call. */
+hattn_status hattn_model_prefill(const hattn_layer_io* layers, int32_t n_layers, int32_t cap,
+                                 const int32_t* pos0, int32_t B, int32_t Sq, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* hattn_status_string(hattn_status status);

@@ -95,10 +95,12 @@ def test_rope_validation(h):
     assert lib.hattn_rope_qk(c, None, None, None, 0, 0, None) == h.HATTN_OK  # empty: no pointers needed
 
 
-def test_append_validation(h):
+@pytest.mark.parametrize("fn", ["hattn_kv_append", "hattn_kv_append_rope"])
+def test_append_validation(h, fn):
     lib = h.lib()
     f, s = _cfg(h, "full"), _cfg(h, "sliding")
     ok = (A, A, A, A)
+    lib = type("L", (), {"hattn_kv_append": getattr(lib, fn)})
     assert lib.hattn_kv_append(f, None, A, A, A, 8, A, 1, 1, None, None) == h.HATTN_ERR_NULL
     assert lib.hattn_kv_append(f, *ok, 8, None, 1, 1, None, None) == h.HATTN_ERR_NULL
     assert lib.hattn_kv_append(f, *ok, 0, A, 1, 1, None, None) == h.HATTN_ERR_SHAPE
@@ -193,3 +195,56 @@ def test_decode_workspace_scales_with_plan(h):
         n = lib.hattn_decode_workspace_bytes(f, B, cap)
         per_chunk = B * 4 * 4 * 258 * 4
         assert n % per_chunk == 0 and n >= per_chunk
+
+
+# ------------------------------------------------------------------ whole-model driver --
+def test_model_schedule_and_kv_bytes_match_oracle_and_pages(h):
+    import oracle as O
+    sched = O.layer_schedule(36)
+    assert [h.model_layer_kind(l) for l in range(36)] == sched
+    assert h.lib().hattn_model_layer_kind(-1) == -1
+    per, total = h.model_kv_bytes(36, 1, 1 << 20)
+    assert total == O.kv_cache_bytes(1 << 20)                        # 9 full + 27 rings
+    assert total == 9 * 4096 * (1 << 20) + 27 * 4096 * 512
+    assert [p == 4096 * (1 << 20) for p in per] == [k == "full" for k in sched]
+    _, t32 = h.model_kv_bytes(36, 32, 131073)
+    assert t32 == 32 * O.kv_cache_bytes(131073)
+
+
+def test_model_validation(h):
+    lib = h.lib()
+    io = (h.LayerIO * 4)()
+    for L in io:
+        for n in ("q", "k", "v", "gate", "k_cache", "v_cache", "out"):
+            setattr(L, n, 0x10000)
+    need = lib.hattn_model_decode_workspace_bytes(4, 2, 1024)
+    assert need > 0 and lib.hattn_model_decode_workspace_bytes(0, 2, 1024) == 0
+    dec = lambda **o: lib.hattn_model_decode(o.get("io", io), o.get("n", 4), o.get("cap", 1024),
+                                             o.get("pos", A), o.get("B", 2), o.get("ws", A),
+                                             o.get("wsb", need), None)
+    assert dec(n=0) == h.HATTN_ERR_SHAPE
+    assert dec(cap=511) == h.HATTN_ERR_SHAPE
+    assert dec(io=None) == h.HATTN_ERR_NULL
+    assert dec(pos=None) == h.HATTN_ERR_NULL
+    assert dec(ws=None) == h.HATTN_ERR_WORKSPACE
+    assert dec(wsb=need - 1) == h.HATTN_ERR_WORKSPACE
+    assert dec(ws=MIS) == h.HATTN_ERR_ALIGN
+    assert dec(B=0) == h.HATTN_OK
+    io[2].v = None
+    assert dec() == h.HATTN_ERR_NULL                 # caught before any layer is enqueued
+    io[2].v = 0x10008
+    assert dec() == h.HATTN_ERR_ALIGN
+    io[2].v = 0x10000
+    io[3].lse = 0x10002
+    assert dec() == h.HATTN_ERR_ALIGN
+    io[3].lse = None
+    pneed = lib.hattn_model_prefill_workspace_bytes(4, 2, 40)
+    assert pneed == 2 * 40 * 4 * 256 * 2
+    pre = lambda **o: lib.hattn_model_prefill(io, 4, 1024, o.get("pos", A), 2, o.get("S", 40),
+                                              o.get("ws", A), o.get("wsb", pneed), None)
+    assert pre(S=-1) == h.HATTN_ERR_SHAPE
+    assert pre(S=0) == h.HATTN_OK
+    assert pre(pos=None) == h.HATTN_ERR_NULL
+    assert pre(wsb=pneed - 16) == h.HATTN_ERR_WORKSPACE
+    assert pre(ws=MIS) == h.HATTN_ERR_ALIGN
+    assert pre(pos=P(0x10002)) == h.HATTN_ERR_ALIGN
