@@ -276,6 +276,86 @@ class SlidingRing1MWorkload:
                      self.ws, rope_q_fused=True)
 
 
+class ModelWorkload:
+    """Workloads 7 and 8: the whole 36-layer schedule on one GPU at a 1M context, through
+    the library's driver (hattn_model_decode / hattn_model_prefill), B=1."""
+
+    def __init__(self, idx: int, device="cuda"):
+        from full_gqa_attention_hattn_amd import hattn
+        self.h = hattn
+        W = synth.WORKLOADS[idx]
+        self.W, self.idx = W, idx
+        self.n_layers = W.params["n_layers"]
+        self.decode = idx == 7
+        if self.decode:
+            self.P, self.S = W.params["decode_pos"], 1          # history 0..P-1, token at P
+        else:
+            self.P, self.S = W.params["cache_len"], W.params["chunk"]
+        self.cap = _cap(self.P + self.S)
+        self.cfg = hattn.preset("full")
+        self.layers, self.rings0 = [], []
+        for l in range(self.n_layers):
+            kind = hattn.model_layer_kind(l)
+            rows = self.cap if kind == "full" else WINDOW
+            filled = self.P if kind == "full" else WINDOW
+            cache = synth.cache_inputs(W.seed, 1, rows, filled, device, layer=l)
+            inp = synth.layer_inputs(W.seed, 1, self.S, device, layer=100 + l)
+            L = dict(kind=kind, q=inp["q"], k=inp["k"], v=inp["v"], gate=inp["gate"],
+                     k_cache=cache["cache_k"], v_cache=cache["cache_v"],
+                     out=torch.empty_like(inp["q"]),
+                     lse=torch.empty(1, self.S, HQ, dtype=torch.float32, device=device))
+            self.layers.append(L)
+            if kind == "sliding" and not self.decode:
+                self.rings0.append((L, L["k_cache"].clone(), L["v_cache"].clone()))
+        self.pos = synth.positions(self.P, 1, device)
+        nbytes = (hattn.model_decode_workspace_bytes(self.n_layers, 1, self.cap) if self.decode
+                  else hattn.model_prefill_workspace_bytes(self.n_layers, 1, self.S))
+        self.ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+        self.kv_per_layer, self.kv_total = hattn.model_kv_bytes(self.n_layers, 1, self.cap)
+        n_full = sum(1 for L in self.layers if L["kind"] == "full")
+        n_sl = self.n_layers - n_full
+        self.stages = Stages(["model_step"])
+        if self.decode:
+            self.prefill_flop = 0
+            self.decode_bytes = KV_BYTES_PER_TOKEN * (n_full * (self.P + 1) + n_sl * WINDOW)
+        else:
+            self.prefill_flop = HQ * FLOP_PER_PAIR * (
+                n_full * prefill_pairs(self.S, self.P, "full")
+                + n_sl * prefill_pairs(self.S, self.P, "sliding"))
+            self.decode_bytes = 0
+
+    def step(self):
+        for L, K0, V0 in self.rings0:      # rings as the previous chunk left them
+            L["k_cache"].copy_(K0)
+            L["v_cache"].copy_(V0)
+        with self.stages.time("model_step"):
+            if self.decode:
+                self.h.model_decode(self.layers, self.cap, self.pos, self.ws)
+            else:
+                self.h.model_prefill(self.layers, self.cap, self.pos, self.ws)
+
+    def graph_ms(self, reps: int = 10):
+        """The decode step captured once as a HIP graph and replayed (launch overhead of the
+        108 kernels gone); mean ms per replay."""
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                self.h.model_decode(self.layers, self.cap, self.pos, self.ws)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+
 def make_workload(idx: int, device="cuda"):
     if idx in (2, 3):
         return PrefillWorkload(idx, device)
@@ -285,6 +365,8 @@ def make_workload(idx: int, device="cuda"):
         return Full1MWorkload(device)
     if idx == 6:
         return SlidingRing1MWorkload(device)
+    if idx in (7, 8):
+        return ModelWorkload(idx, device)
     raise ValueError(f"no bench workload {idx} (1 is the parity-only tiny case)")
 
 
@@ -317,6 +399,45 @@ def cpu_baseline(wl, budget_s: float):
         return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                 "sample": f"prefill rows {done} of the 4096-query chunk over the full "
                           f"{wl.L0 + wl.C}-token cache, all 16 heads ({dt:.1f} s)"}
+    if isinstance(wl, ModelWorkload):
+        # layer 3 (the first full layer) and layer 0 (sliding), the oracle as it stands
+        full, sl = wl.layers[3], wl.layers[0]
+        t0 = time.perf_counter()
+        if wl.decode:
+            done, nbytes = [], 0
+            for L in (sl, full):
+                kind = L["kind"]
+                rows = wl.P if kind == "full" else WINDOW
+                kc = L["k_cache"][0, :max(rows, WINDOW) if kind == "sliding" else wl.P + 1].cpu().float()
+                vc = L["v_cache"][0, :kc.shape[0]].cpu().float()
+                _, kn = O.rope_qk(None, L["k"][0].cpu(), wl.P, kind)
+                slot = wl.P if kind == "full" else wl.P % WINDOW
+                kc[slot] = kn[0]
+                vc[slot] = L["v"][0, 0].cpu().float()
+                O.decode(L["q"][0, 0].cpu(), kc, vc, L["gate"][0, 0].cpu(), wl.P, kind)
+                nbytes += KV_BYTES_PER_TOKEN * ((wl.P + 1) if kind == "full" else WINDOW)
+                done.append(kind)
+            dt = time.perf_counter() - t0
+            return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                    "sample": f"decode of layer 0 (sliding) and layer 3 (full, 2^20+1 keys), "
+                              f"cache copy to host included ({dt:.1f} s)"}
+        kc = full["k_cache"][0, :wl.P].cpu().float()
+        vc = full["v_cache"][0, :wl.P].cpu().float()
+        _, kr = O.rope_qk(None, full["k"][0].cpu(), wl.P, "full")
+        kc = torch.cat([kc, kr])
+        vc = torch.cat([vc, full["v"][0].cpu().float()])
+        done, flop = [], 0
+        for r in (wl.S - 1, wl.S - 2):
+            O.prefill(full["q"][0].cpu(), kc, vc, full["gate"][0].cpu(), wl.P, "full",
+                      rows=torch.tensor([r]))
+            flop += HQ * FLOP_PER_PAIR * (wl.P + r + 1)
+            done.append(r)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"prefill rows {done} of layer 3 (full) over the 2^20-token cache, "
+                          f"all 16 heads ({dt:.1f} s)"}
     if isinstance(wl, SlidingRing1MWorkload):
         rows = list(range(wl.C - 1, wl.C - 257, -1))
         q, g = wl.q[0].cpu(), wl.gate[0].cpu()
@@ -418,13 +539,43 @@ def copy_calibration(mib: int):
     del src, dst
 
 
+def model_fields(rec, wl, ms, stage_ms):
+    """JSON fields of the whole-model workloads: the driver's step is timed as one unit
+    (HIP events around the one library call), so the roofline line is the step's own
+    rate over all its kernels, a lower bound for the dominant kernel."""
+    step_ms = stage_ms["model_step"]
+    rec["kv_cache_bytes"] = {"total": wl.kv_total,
+                             "full_layer": max(wl.kv_per_layer),
+                             "sliding_layer": min(wl.kv_per_layer),
+                             "n_full": sum(1 for L in wl.layers if L["kind"] == "full"),
+                             "n_sliding": sum(1 for L in wl.layers if L["kind"] == "sliding")}
+    if wl.decode:
+        rec["value"] = wl.decode_bytes / (ms * 1e-3) / 1e9
+        rec["unit"] = "GB/s"
+        ach = wl.decode_bytes / (step_ms * 1e-3) / 1e9
+        g_ms = wl.graph_ms()
+        rec["graph_ms_per_step"] = g_ms
+        rec["graph_GBps"] = wl.decode_bytes / (g_ms * 1e-3) / 1e9
+        rec["decode_steps_per_s"] = 1e3 / g_ms
+        rec["roofline"] = {"bound": "hbm", "kernel": "hattn_model_decode step (all kernels)",
+                           "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": ach / PEAK_HBM_GBPS, "traffic": None}
+    else:
+        rec["value"] = wl.prefill_flop / (ms * 1e-3) / 1e12
+        rec["unit"] = "TFLOP/s"
+        ach = wl.prefill_flop / (step_ms * 1e-3) / 1e12
+        rec["roofline"] = {"bound": "mfma", "kernel": "hattn_model_prefill step (all kernels)",
+                           "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+
+
 # ------------------------------------------------------------------------------ main --
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -459,7 +610,9 @@ def main():
            "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16; no weights needed)"}
     stage_ms = {k: st.mean_ms(k) for k in st.t if st.t[k]}
     rec["stage_ms"] = stage_ms
-    if wl.prefill_flop:
+    if isinstance(wl, ModelWorkload):
+        model_fields(rec, wl, ms, stage_ms)
+    elif wl.prefill_flop:
         pf_ms = stage_ms["prefill"]
         rec["value"] = wl.prefill_flop / (ms * 1e-3) / 1e12
         rec["unit"] = "TFLOP/s"
@@ -473,7 +626,7 @@ def main():
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("prefill.hip", tr_name)}
-    if wl.decode_bytes:
+    if wl.decode_bytes and not isinstance(wl, ModelWorkload):
         dec_ms = sum(stage_ms.get(k, 0.0) for k in ("decode", "decode_full", "decode_sliding"))
         if isinstance(wl, MixedDecodeWorkload):
             dec_ms = stage_ms["decode_full"] + 3 * stage_ms["decode_sliding"]

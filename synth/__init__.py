@@ -125,6 +125,15 @@ WORKLOADS = {
                 "against the ring, the chunk appended, then one ring decode at 1048576",
                 1240, dict(B=1, ring_pos=1044480, chunk=4096, decode_pos=1 << 20,
                            window=512)),
+    7: Workload(7, "model_36l_1m_decode",
+                "36-layer hybrid schedule (9 full + 27 sliding), B=1: one decode step at "
+                "position 1048576; full caches hold positions 0..1048575, rings the last 512",
+                1241, dict(B=1, n_layers=36, decode_pos=1 << 20)),
+    8: Workload(8, "model_36l_1m_chunk4096",
+                "36-layer hybrid schedule (9 full + 27 sliding), B=1: one prefill chunk of "
+                "4096 queries at 1044480..1048575; full caches hold positions 0..1044479, "
+                "rings 1043968..1044479",
+                1242, dict(B=1, n_layers=36, cache_len=1044480, chunk=4096)),
 }
 
 

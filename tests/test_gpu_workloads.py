@@ -201,3 +201,52 @@ def test_sliding_ring_1m_chunk_and_decode(bench):
     yd, ld = O.decode(_cpu(wl.qd[0, 0]), ring_k, ring_v, _cpu(wl.gd[0, 0]), wl.pd, "sliding")
     check_outputs(_cpu(wl.outd[0, 0]), _cpu(wl.lsed[0, 0]), yd, ld, "w6 ring decode p=2^20")
     _free(wl)
+
+
+def _oracle_layer_rows(wl, L, rows):
+    """Oracle prefill rows of one layer of a whole-model chunk workload (B=1)."""
+    kind = L["kind"]
+    _, kr = O.rope_qk(None, _cpu(L["k"][0]), wl.P, kind)
+    if kind == "full":
+        kc = torch.cat([_cpu(L["k_cache"][0, :wl.P]).float(), kr])
+        vc = torch.cat([_cpu(L["v_cache"][0, :wl.P]).float(), _cpu(L["v"][0]).float()])
+        return O.prefill(_cpu(L["q"][0]), kc, vc, _cpu(L["gate"][0]), wl.P, kind, rows=rows)
+    K0, V0 = next((k, v) for (LL, k, v) in wl.rings0 if LL is L)
+    return O.prefill_ring(_cpu(L["q"][0]), kr, _cpu(L["v"][0]), _cpu(K0[0]), _cpu(V0[0]),
+                          _cpu(L["gate"][0]), wl.P, rows=rows)
+
+
+def test_model_36_layers_1m_chunk(bench):
+    say("workload 8: 36-layer chunk of 4096 at 1M")
+    wl = bench.make_workload(8)
+    wl.step()
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 511, 512, 2047, 4094, 4095])
+    for l in (0, 3, 34, 35):          # sliding and full, first and last of the schedule
+        L = wl.layers[l]
+        y, lse = _oracle_layer_rows(wl, L, rows)
+        check_outputs(_cpu(L["out"][0])[rows], _cpu(L["lse"][0])[rows], y, lse,
+                      f"w8 layer {l} ({L['kind']})")
+    _free(wl)
+
+
+def test_model_36_layers_1m_decode(bench):
+    say("workload 7: 36-layer decode at 2^20")
+    wl = bench.make_workload(7)
+    wl.step()
+    torch.cuda.synchronize()
+    p = wl.P
+    for l in (0, 3, 34, 35):
+        L = wl.layers[l]
+        kind = L["kind"]
+        _, kn = O.rope_qk(None, _cpu(L["k"][0]), p, kind)
+        if kind == "full":
+            kc = torch.cat([_cpu(L["k_cache"][0, :p]).float(), kn])
+            vc = torch.cat([_cpu(L["v_cache"][0, :p]).float(), _cpu(L["v"][0]).float()])
+        else:
+            kc, vc = _cpu(L["k_cache"][0]).float(), _cpu(L["v_cache"][0]).float()
+            kc[p % 512] = kn[0]
+            vc[p % 512] = _cpu(L["v"][0, 0]).float()
+        y, lse = O.decode(_cpu(L["q"][0, 0]), kc, vc, _cpu(L["gate"][0, 0]), p, kind)
+        check_outputs(_cpu(L["out"][0, 0]), _cpu(L["lse"][0, 0]), y, lse, f"w7 layer {l} ({kind})")
+    _free(wl)
