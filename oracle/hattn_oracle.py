@@ -290,6 +290,90 @@ def decode(q, k_cache, v_cache, gate, pos: int, kind, *, q_rotated: bool = False
     return y[0], lse[0]
 
 
+# --- 8-bit KV cache ---------------------------------------------------------------------
+# [T5] §3.2 "Deployment steps and key parameters": to fit a 1M context the deployment
+# also quantizes the KV cache (8- or 4-bit), trading some precision for memory.  The
+# format here is this library's own: OCP FP8 E4M3 ("e4m3fn": sign, 4 exponent bits with
+# bias 7, 3 mantissa bits, subnormals, no infinities, codes 0x7F / 0xFF are NaN, largest
+# finite 448) with one fp32 scale per (token, KV head): scale = amax / 448, code =
+# e4m3(x / scale) rounded to nearest, ties to even.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: torch.Tensor) -> torch.Tensor:
+    """Value of each uint8 E4M3 code, fp32, from the format's definition."""
+    c = codes.to(torch.int64)
+    sign = torch.where((c & 0x80) != 0, -1.0, 1.0).to(torch.float64)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).to(torch.float64)
+    normal = torch.ldexp(1.0 + m / 8.0, (e - 7).to(torch.int32))
+    sub = m / 8.0 * 2.0 ** -6
+    v = sign * torch.where(e == 0, sub, normal)
+    v = torch.where((c & 0x7F) == 0x7F, torch.full_like(v, float("nan")), v)
+    return v.to(torch.float32)
+
+
+_E4M3_POS = None
+
+
+def _e4m3_positive_table():
+    """The 127 non-negative finite codes 0x00..0x7E and their values, ascending."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        codes = torch.arange(0, 0x7F, dtype=torch.int64)
+        _E4M3_POS = (codes, e4m3_decode(codes).to(torch.float64))
+    return _E4M3_POS
+
+
+def e4m3_encode(x: torch.Tensor) -> torch.Tensor:
+    """Nearest E4M3 code of each fp32 value, ties to the even code; |x| > 448 saturates
+    to 448 (the quantizer never produces such values; see kv_quantize)."""
+    codes, vals = _e4m3_positive_table()
+    xf = x.to(torch.float64)
+    a = xf.abs().clamp(max=E4M3_MAX).reshape(-1)
+    hi = torch.searchsorted(vals, a).clamp(max=len(vals) - 1)   # first value >= a
+    lo = (hi - 1).clamp(min=0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    idx = torch.where(pick_hi, hi, lo)
+    out = codes[idx]
+    neg = (xf.reshape(-1) < 0) | ((xf.reshape(-1) == 0) & torch.signbit(xf.reshape(-1)))
+    out = torch.where(neg, out | 0x80, out)
+    return out.to(torch.uint8).reshape(x.shape)
+
+
+def kv_quantize(x: torch.Tensor):
+    """Quantize keys or values x [n, Hkv, D] (bf16 or fp32 values) to E4M3 codes with one
+    fp32 scale per (token, head): scale = fp32(amax / 448), code = e4m3(fp32(x / scale))
+    (0 when the row is all zero).  Returns (codes uint8 [n, Hkv, D], scale fp32 [n, Hkv])."""
+    xf = x.to(torch.float32)
+    amax = xf.abs().amax(dim=-1)
+    scale = amax / torch.tensor(E4M3_MAX, dtype=torch.float32)      # fp32, correctly rounded
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    y = (xf / safe[..., None]).clamp(-E4M3_MAX, E4M3_MAX)
+    y = torch.where(scale[..., None] > 0, y, torch.zeros_like(y))
+    return e4m3_encode(y), scale
+
+
+def kv_dequantize(codes: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """codes [n, Hkv, D], scale [n, Hkv] -> fp32 values code_value * scale."""
+    return e4m3_decode(codes) * scale[..., None].to(torch.float32)
+
+
+def decode_kv8(q, k_codes, v_codes, k_scale, v_scale, gate, pos: int, kind, *,
+               q_rotated: bool = False):
+    """decode() over a cache held as E4M3 codes with per-(token, head) scales: the same
+    attention on the dequantized keys and values.  Cache layouts as in decode();
+    k_scale / v_scale [cap, Hkv]."""
+    return decode(q, kv_dequantize(k_codes, k_scale), kv_dequantize(v_codes, v_scale), gate,
+                  pos, kind, q_rotated=q_rotated)
+
+
+def kv8_bytes_per_token_layer(n_kv_heads: int = N_KV_HEADS, head_dim: int = HEAD_DIM) -> int:
+    """K and V codes (1 byte each) plus their two fp32 scales per head."""
+    return 2 * n_kv_heads * head_dim + 2 * n_kv_heads * 4
+
+
 # --- KV memory arithmetic ([T1] "Doing the arithmetic first", "Hybrid attention") ----
 def kv_bytes_per_token_layer(n_kv_heads: int = N_KV_HEADS, head_dim: int = HEAD_DIM,
                              bytes_per_elem: int = 2) -> int:
@@ -330,5 +414,7 @@ __all__ = [
     "rope_qk", "append_slots", "kv_append", "ring_positions", "prefill", "prefill_ring",
     "decode",
     "kv_bytes_per_token_layer", "kv_cache_bytes", "attention_pairs_prefill",
+    "E4M3_MAX", "e4m3_decode", "e4m3_encode", "kv_quantize", "kv_dequantize", "decode_kv8",
+    "kv8_bytes_per_token_layer",
     "sdpa_flops_per_pair",
 ]

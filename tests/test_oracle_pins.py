@@ -434,6 +434,83 @@ def test_ring_prefill_brute_force_slot_lookup():
             assert abs(float(lse[i, h]) - (sc.max() + math.log(w.sum()))) < 1e-5
 
 
+# ---------------------------------------------------------------- 8-bit KV cache --
+def test_e4m3_code_values_closed_form():
+    """Code values from the E4M3 definition: bias 7, 3 mantissa bits, subnormals below
+    2^-6, largest finite 448, 0x7F / 0xFF NaN."""
+    codes = torch.tensor([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x77, 0x7E, 0x80, 0xB8, 0xFE],
+                         dtype=torch.uint8)
+    want = [0.0, 2 ** -9, 7 * 2 ** -9, 2 ** -6, 1.0, 1.5, 240.0, 448.0, -0.0, -1.0, -448.0]
+    got = O.e4m3_decode(codes).tolist()
+    assert got == want
+    assert math.copysign(1, O.e4m3_decode(torch.tensor([0x80], dtype=torch.uint8))[0]) == -1
+    nan = O.e4m3_decode(torch.tensor([0x7F, 0xFF], dtype=torch.uint8))
+    assert bool(torch.isnan(nan).all())
+
+
+def test_e4m3_encode_matches_library_and_round_trips():
+    """Encoding matches torch's float8_e4m3fn conversion (round to nearest, ties to even)
+    on random values and on every midpoint between neighbouring codes; every finite code
+    decodes and re-encodes to itself."""
+    g = torch.Generator().manual_seed(90)
+    x = torch.randn(200000, generator=g) * torch.exp2(torch.randint(-12, 9, (200000,), generator=g).float())
+    x = x.clamp(-448, 448)
+    fin = torch.tensor([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=torch.uint8)
+    vals = O.e4m3_decode(fin).double()
+    pos = torch.sort(vals[vals > 0]).values
+    mids = ((pos[1:] + pos[:-1]) / 2).float()                 # exact ties in fp32
+    for t in (x, mids, -mids):
+        assert torch.equal(O.e4m3_encode(t), t.to(torch.float8_e4m3fn).view(torch.uint8))
+    assert torch.equal(O.e4m3_encode(O.e4m3_decode(fin)), fin)
+
+
+def test_kv_quantize_scale_and_error_bound():
+    g = torch.Generator().manual_seed(91)
+    x = (torch.randn(64, 4, 256, generator=g) * 3).to(torch.bfloat16)
+    x[5, 2] = 0                                                # an all-zero row
+    codes, scale = O.kv_quantize(x)
+    xf = x.float()
+    amax = xf.abs().amax(-1)
+    assert torch.equal(scale, amax / 448.0)
+    assert float(scale[5, 2]) == 0 and bool((codes[5, 2] == 0).all())
+    # the largest element of every non-zero row lands on +-448 exactly
+    idx = xf.abs().argmax(-1, keepdim=True)
+    top = torch.gather(O.e4m3_decode(codes).abs(), -1, idx).squeeze(-1)
+    assert bool((top[amax > 0] == 448.0).all())
+    # half an E4M3 step: 2^-4 relative on normals, 2^-10 * scale absolute below them
+    deq = O.kv_dequantize(codes, scale)
+    err = (deq - xf).abs()
+    bound = torch.maximum(2 ** -4 * xf.abs(), 2 ** -10 * scale[..., None]) * (1 + 1e-6)
+    assert bool((err <= bound).all())
+    assert O.kv8_bytes_per_token_layer() == 2080
+
+
+@pytest.mark.parametrize("kind", ["sliding", "full"])
+def test_decode_kv8_is_decode_of_dequantized_cache(kind):
+    """decode_kv8 equals decode() on the dequantized cache, and stays within the noise
+    that 3-bit mantissas put on N(0,1) data of the bf16 decode (a dropped or misapplied
+    scale would move it by orders of magnitude)."""
+    S, pos = 700, 699
+    base = synth.layer_inputs(92, 1, S)
+    q, k, v, g = (base[n][0] for n in ("q", "k", "v", "gate"))
+    _, kr = O.rope_qk(None, k, 0, kind)
+    kr = kr.to(torch.bfloat16)
+    if kind == "sliding":
+        kc = torch.zeros(512, 4, 256, dtype=torch.bfloat16)
+        vc = torch.zeros_like(kc)
+        O.kv_append(kc, vc, kr, v, 0, kind)
+    else:
+        kc, vc = kr, v
+    kq, ks = O.kv_quantize(kc)
+    vq, vs = O.kv_quantize(vc)
+    y8, l8 = O.decode_kv8(q[pos], kq, vq, ks, vs, g[pos], pos, kind)
+    yd, ld = O.decode(q[pos], O.kv_dequantize(kq, ks), O.kv_dequantize(vq, vs), g[pos], pos, kind)
+    assert torch.equal(y8, yd) and torch.equal(l8, ld)
+    y, l = O.decode(q[pos], kc, vc, g[pos], pos, kind)
+    rel = (y8 - y).norm(dim=-1) / y.norm(dim=-1)
+    assert float(rel.max()) < 0.08 and float((l8 - l).abs().max()) < 0.02
+
+
 # ------------------------------------------------------------------ closed forms --
 def test_kv_memory_matches_page_figures():
     m = json.loads((GOLD / "kv_memory.json").read_text())
