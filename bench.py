@@ -356,6 +356,53 @@ class ModelWorkload:
         return a.elapsed_time(b) / reps
 
 
+class Kv8DecodeWorkload:
+    """Workloads 9 and 10: full-layer decode over the 8-bit KV cache.  The history is drawn
+    in bf16 and quantized once by the library's own append (untimed); a step appends the
+    new token (rotated and quantized) and decodes it."""
+
+    def __init__(self, idx: int, device="cuda", keep_source: bool = False):
+        from full_gqa_attention_hattn_amd import hattn
+        self.h = hattn
+        W = synth.WORKLOADS[idx]
+        self.W = W
+        B, P = W.params["B"], W.params["decode_pos"]
+        self.B, self.P = B, P
+        self.cap = _cap(P + 1)
+        self.cfg = hattn.preset("full")
+        src = synth.cache_inputs(W.seed, B, self.cap, P, device, layer=0)
+        self.K = torch.empty(B, self.cap, HKV, D, dtype=torch.uint8, device=device)
+        self.V = torch.empty_like(self.K)
+        self.Ks = torch.zeros(B, HKV, self.cap, dtype=torch.float32, device=device)
+        self.Vs = torch.zeros_like(self.Ks)
+        zero = synth.positions(0, B, device)
+        # every row (those past P are zero and quantize to zero codes and scales)
+        hattn.kv_append_fp8(self.cfg, src["cache_k"], src["cache_v"], self.K, self.V, self.Ks,
+                            self.Vs, zero)
+        torch.cuda.synchronize()
+        self.source = src if keep_source else None
+        del src
+        new = synth.layer_inputs(W.seed, B, 1, device, layer=1)
+        self.q, self.k, self.v, self.gate = new["q"], new["k"], new["v"], new["gate"]
+        self.pos = synth.positions(P, B, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(B, 1, HQ, dtype=torch.float32, device=device)
+        self.ws = hattn.alloc_workspace(self.cfg, B, self.cap, device)
+        self.stages = Stages(["append", "decode"])
+        self.prefill_flop = 0
+        self.kv8_bytes_per_token = 2 * HKV * D + 2 * HKV * 4
+        self.decode_bytes = B * self.kv8_bytes_per_token * (P + 1)
+
+    def step(self):
+        h = self.h
+        with self.stages.time("append"):
+            h.kv_append_fp8(self.cfg, self.k, self.v, self.K, self.V, self.Ks, self.Vs, self.pos,
+                            rope_k=True)
+        with self.stages.time("decode"):
+            h.decode_fp8(self.cfg, self.q, self.K, self.V, self.Ks, self.Vs, self.pos, self.gate,
+                         self.out, self.lse, self.ws, rope_q_fused=True)
+
+
 def make_workload(idx: int, device="cuda"):
     if idx in (2, 3):
         return PrefillWorkload(idx, device)
@@ -367,6 +414,8 @@ def make_workload(idx: int, device="cuda"):
         return SlidingRing1MWorkload(device)
     if idx in (7, 8):
         return ModelWorkload(idx, device)
+    if idx in (9, 10):
+        return Kv8DecodeWorkload(idx, device)
     raise ValueError(f"no bench workload {idx} (1 is the parity-only tiny case)")
 
 
@@ -399,6 +448,22 @@ def cpu_baseline(wl, budget_s: float):
         return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                 "sample": f"prefill rows {done} of the 4096-query chunk over the full "
                           f"{wl.L0 + wl.C}-token cache, all 16 heads ({dt:.1f} s)"}
+    if isinstance(wl, Kv8DecodeWorkload):
+        t0 = time.perf_counter()
+        nbytes, done = 0, 0
+        for b in range(wl.B):
+            n = wl.P + 1
+            kq, vq = wl.K[b, :n].cpu(), wl.V[b, :n].cpu()
+            ks, vs = wl.Ks[b, :, :n].cpu().T, wl.Vs[b, :, :n].cpu().T
+            O.decode_kv8(wl.q[b, 0].cpu(), kq, vq, ks, vs, wl.gate[b, 0].cpu(), wl.P, "full")
+            nbytes += wl.kv8_bytes_per_token * n
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"8-bit full-layer decode of {done} of {wl.B} sequences, cache copy "
+                          f"to host included ({dt:.1f} s)"}
     if isinstance(wl, ModelWorkload):
         # layer 3 (the first full layer) and layer 0 (sliding), the oracle as it stands
         full, sl = wl.layers[3], wl.layers[0]
@@ -575,7 +640,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", type=int, default=5, choices=list(range(2, 11)))
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -626,7 +691,21 @@ def main():
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("prefill.hip", tr_name)}
-    if wl.decode_bytes and not isinstance(wl, ModelWorkload):
+    if isinstance(wl, Kv8DecodeWorkload):
+        dec_ms = stage_ms["decode"]
+        gbps = wl.decode_bytes / (dec_ms * 1e-3) / 1e9
+        rec["value"] = wl.decode_bytes / (ms * 1e-3) / 1e9
+        rec["unit"] = "GB/s"
+        rec["decode_GBps"] = gbps
+        rec["decode_frac_hbm_peak"] = gbps / PEAK_HBM_GBPS
+        rec["keys_per_s"] = wl.B * (wl.P + 1) / (dec_ms * 1e-3)
+        rec["kv_bytes_per_token_layer"] = wl.kv8_bytes_per_token
+        name = {9: "decode_fp8_full_1m", 10: "decode_fp8_full_b32_p131072"}[args.workload]
+        rec["roofline"] = {"bound": "hbm", "kernel": "decode_split_fp8_kernel+combine",
+                           "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": gbps / PEAK_HBM_GBPS,
+                           "traffic": measured_traffic("decode.hip", name)}
+    elif wl.decode_bytes and not isinstance(wl, ModelWorkload):
         dec_ms = sum(stage_ms.get(k, 0.0) for k in ("decode", "decode_full", "decode_sliding"))
         if isinstance(wl, MixedDecodeWorkload):
             dec_ms = stage_ms["decode_full"] + 3 * stage_ms["decode_sliding"]

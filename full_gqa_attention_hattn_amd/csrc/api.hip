@@ -207,6 +207,63 @@ hattn_status hattn_prefill_ring(const hattn_layer_cfg* cfg, const void* q, const
       cfg->window, (flags & HATTN_ROPE_Q_FUSED) != 0, tab, scale_log2e(cfg), as_stream(stream)));
 }
 
+hattn_status hattn_kv_append_fp8(const hattn_layer_cfg* cfg, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache, float* k_scale,
+                                 float* v_scale, int32_t cap, const int32_t* pos0, int32_t B,
+                                 int32_t n, int32_t* slots_out, uint32_t flags, void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (B < 0 || n < 0 || cap < 1) return HATTN_ERR_SHAPE;
+  if ((flags & ~(uint32_t)HATTN_KV8_ROPE_K) != 0) return HATTN_ERR_UNSUPPORTED;
+  if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return HATTN_ERR_RANGE;
+  const long long ntok = (long long)B * n;
+  if (ntok == 0) return HATTN_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !pos0)
+    return HATTN_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(k_scale) || !aligned4(v_scale) || !aligned4(pos0) ||
+      (slots_out && !aligned4(slots_out)))
+    return HATTN_ERR_ALIGN;
+  if (ntok * 256 > kMaxWorkItems || (long long)B * cap >= (1LL << 40)) return HATTN_ERR_SHAPE;
+  const hattn::RopeTable tab = rope_table(cfg);
+  return hip_status(hattn::launch_kv_append_fp8(
+      static_cast<const hattn::bf16_t*>(k_new), static_cast<const hattn::bf16_t*>(v_new),
+      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale, cap, pos0,
+      B, n, cfg->kind == HATTN_SLIDING ? cfg->window : 0, slots_out,
+      (flags & HATTN_KV8_ROPE_K) ? &tab : nullptr, as_stream(stream)));
+}
+
+hattn_status hattn_decode_fp8(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              int32_t cap, const int32_t* pos, int32_t B, const void* gate,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              uint32_t flags, void* stream) {
+  hattn_status st = check_cfg(cfg);
+  if (st != HATTN_OK) return st;
+  if (B < 0 || cap < 1) return HATTN_ERR_SHAPE;
+  if ((flags & ~(uint32_t)HATTN_ROPE_Q_FUSED) != 0) return HATTN_ERR_UNSUPPORTED;
+  if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return HATTN_ERR_RANGE;
+  if (B == 0) return HATTN_OK;
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !pos || !gate || !out)
+    return HATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(k_scale) ||
+      !aligned4(v_scale) || !aligned2(out) || !aligned2(gate) || !aligned4(pos) ||
+      (lse && !aligned4(lse)))
+    return HATTN_ERR_ALIGN;
+  if (B > 65535 || (long long)B * cap >= (1LL << 40)) return HATTN_ERR_SHAPE;
+  const hattn::DecodePlan plan = hattn::decode_plan(B, decode_max_keys(cfg, cap));
+  const size_t need = hattn::decode_workspace_bytes(B, plan);
+  if (workspace == nullptr || workspace_bytes < need) return HATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
+  const hattn::RopeTable tab = rope_table(cfg);
+  return hip_status(hattn::launch_decode_fp8(
+      static_cast<const hattn::bf16_t*>(q), static_cast<const uint8_t*>(k_cache),
+      static_cast<const uint8_t*>(v_cache), k_scale, v_scale, cap, pos, B,
+      static_cast<const hattn::bf16_t*>(gate), static_cast<hattn::bf16_t*>(out), lse,
+      cfg->kind == HATTN_SLIDING ? cfg->window : 0, (flags & HATTN_ROPE_Q_FUSED) != 0, tab,
+      scale_log2e(cfg), plan, workspace, as_stream(stream)));
+}
+
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
   if (check_cfg(cfg) != HATTN_OK || B < 0 || cap < 1) return 0;
   if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return 0;

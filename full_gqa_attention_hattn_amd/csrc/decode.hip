@@ -98,22 +98,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
 
   for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
+    // Keys past k_end read row k_end - 1 instead (their scores are masked to -inf, so those
+    // values meet a zero probability): unconditional loads the compiler can count, so the
+    // QK chain waits only for K while V is still in flight.
     bf16x8 kf[2][8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int key = k0 + 16 * blk + n16;
-      const bool ok = key < k_end;
+      const int key = min(k0 + 16 * blk + n16, k_end - 1);
       const bf16_t* kr = kb + (long long)key * rs + 8 * g;
 #pragma unroll
-      for (int dc = 0; dc < 8; ++dc)
-        kf[blk][dc] = ok ? *reinterpret_cast<const bf16x8*>(kr + 32 * dc) : bf16x8{};
+      for (int dc = 0; dc < 8; ++dc) kf[blk][dc] = *reinterpret_cast<const bf16x8*>(kr + 32 * dc);
     }
     uint4 vv[16];
 #pragma unroll
     for (int kp = 0; kp < 16; ++kp) {
-      const int key = k0 + 2 * kp + half;
-      vv[kp] = key < k_end ? *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 8 * dg)
-                           : uint4{0u, 0u, 0u, 0u};
+      const int key = min(k0 + 2 * kp + half, k_end - 1);
+      vv[kp] = *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 8 * dg);
     }
 
     f32x4 s[2] = {f32x4{}, f32x4{}};
@@ -209,6 +209,224 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
+// 8-bit KV variant of decode_split_kernel: the caches hold E4M3 codes [B, cap, 4, 256]
+// with fp32 scales [B, 4, cap] per (token, KV head).  Same grid, waves and partials.
+//   * QK: a lane's K fragment (8 codes of one key) is widened exactly to bf16 with the
+//     hardware conversion (scale 1), the bf16 MFMA runs as before, and the key's scale
+//     multiplies its score: sum_d q_d (c_d s) = s sum_d q_d c_d.
+//   * PV: the value scale of key j is folded into its probability before the broadcast
+//     (sum_j p_j s_j c_j); lane (kq, dg16) accumulates keys kq, kq + 4, .. of the step over
+//     dims 16 dg16 .. +15, and the 4 key phases are summed at the end of the chunk.
+// The softmax sum uses the unscaled probabilities.  [T5] §3.2 "Deployment steps and key
+// parameters" (quantized KV cache for the 1M context).
+template <bool kSliding>
+__global__ __launch_bounds__(256) void decode_split_fp8_kernel(
+    const bf16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const float* __restrict__ ksc, const float* __restrict__ vsc, int cap,
+    const int* __restrict__ pos, int window, int chunk, int nchunks, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml, int rope_q, RopeTable tab, float sl2) {
+  constexpr int kNdc = kSliding ? 4 : 1;
+  __shared__ __attribute__((aligned(16))) float p_lds[kHkv][kStep][4];
+
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, kvh = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;    // MFMA view: column (head) and k-group
+  const int kq = lane >> 4, dg = lane & 15;    // PV view: key phase and 16-dim group
+  const int p = pos[b];
+  int kv_len = kSliding ? min(p + 1, window) : p + 1;
+  kv_len = max(0, min(kv_len, cap));
+  const int k_begin = c * chunk;
+  const int k_end = min(kv_len, k_begin + chunk);
+
+  const bool qlane = n16 < kGroup;
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = q + ((long long)b * kHq + kvh * kGroup + (qlane ? n16 : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+  }
+  if (rope_q && qlane) {
+#pragma unroll
+    for (int dc = 0; dc < kNdc; ++dc) {
+      const bf16x8 xa = qf[dc], xb = qf[dc + kNdc];
+      f32x4 ya0, ya1, yb0, yb1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sv, cv;
+        sincos_angle(rope_angle(p, tab.inv_freq[32 * dc + 8 * g + e]), &sv, &cv);
+        float ya, yb;
+        rope_pair((float)xa[e], (float)xb[e], cv, sv, &ya, &yb);
+        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
+      }
+      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
+      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
+      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      qf[dc + kNdc] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    }
+  }
+
+  constexpr long long rs = kHkv * kD;  // bytes per cache row (4 heads x 256 codes)
+  const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
+  const uint8_t* kb = kc + kv_off;
+  const uint8_t* vb = vc + kv_off;
+  const float* ks = ksc + ((long long)b * kHkv + kvh) * cap;
+  const float* vs = vsc + ((long long)b * kHkv + kvh) * cap;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[kGroup][16];
+#pragma unroll
+  for (int hl = 0; hl < kGroup; ++hl)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[hl][e] = 0.f;
+
+  // Step k0's K codes, scales and V codes.  Keys past k_end read row k_end - 1 (masked
+  // scores, zero probabilities), so the loads are unconditional and the compiler can count
+  // them; each array is refilled for the next step as soon as this step has consumed it
+  // (the last step reloads its final row), keeping loads in flight during the arithmetic.
+  uint2 kraw[2][8];
+  float kscale[2][4], vscale[2][4];
+  uint4 vraw[8];
+  auto load_k = [&](int k0) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = min(k0 + 16 * blk + n16, k_end - 1);
+      const uint8_t* kr = kb + (long long)key * rs + 8 * g;
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) kraw[blk][dc] = *reinterpret_cast<const uint2*>(kr + 32 * dc);
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = min(k0 + 16 * blk + 4 * g + j, k_end - 1);
+        kscale[blk][j] = ks[key];
+        vscale[blk][j] = vs[key];
+      }
+  };
+  auto load_v = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = min(k0 + kq + 4 * i, k_end - 1);
+      vraw[i] = *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 16 * dg);
+    }
+  };
+  if (k_begin < k_end) {
+    load_k(k_begin);
+    load_v(k_begin);
+  }
+  for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
+    const int kn = min(k0 + kStep, k_end - 1);
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint2 w = kraw[blk][dc];
+        const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+        const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+        const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+        const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+        const bf16x8 kf = bf16x8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+        sacc[blk] = mfma16(kf, qf[dc], sacc[blk]);
+      }
+    }
+    float mloc = -INFINITY;
+    float sv[2][4], vsc[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + 16 * blk + 4 * g + j;
+        const float v = key < k_end ? sacc[blk][j] * kscale[blk][j] * sl2 : -INFINITY;
+        sv[blk][j] = v;
+        vsc[blk][j] = vscale[blk][j];
+        mloc = fmaxf(mloc, v);
+      }
+    load_k(kn);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rsum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pj = fast_exp2(sv[blk][j] - m_use);
+        sv[blk][j] = pj;
+        rsum += pj;
+      }
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+
+    if (qlane) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          p_lds[kvh][16 * blk + 4 * g + j][n16] = sv[blk][j] * vsc[blk][j];
+    }
+    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
+    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
+    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      o[0][e] *= a0;
+      o[1][e] *= a1;
+      o[2][e] *= a2;
+      o[3][e] *= a3;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(&p_lds[kvh][kq + 4 * i][0]);
+      const uint32_t vw[4] = {vraw[i].x, vraw[i].y, vraw[i].z, vraw[i].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[w], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[w], true);
+        const float v4[4] = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int hl = 0; hl < kGroup; ++hl) o[hl][4 * w + e] += pv[hl] * v4[e];
+      }
+    }
+    load_v(kn);
+    wave_lds_fence();
+  }
+
+  // Sum the 4 key phases, then the softmax sums over the 4 k-groups.
+#pragma unroll
+  for (int hl = 0; hl < kGroup; ++hl)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      o[hl][e] += __shfl_xor(o[hl][e], 16);
+      o[hl][e] += __shfl_xor(o[hl][e], 32);
+    }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  const long long part = ((long long)(b * kHkv + kvh) * nchunks + c) * kGroup;
+  if (kq == 0) {
+#pragma unroll
+    for (int hl = 0; hl < kGroup; ++hl) {
+      float* dst = ws_o + (part + hl) * kD + 16 * dg;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<f32x4*>(dst + 4 * e4) =
+            f32x4{o[hl][4 * e4], o[hl][4 * e4 + 1], o[hl][4 * e4 + 2], o[hl][4 * e4 + 3]};
+    }
+  }
+  if (lane < kGroup) {
+    ws_ml[(part + lane) * 2] = m_run;
+    ws_ml[(part + lane) * 2 + 1] = l_run;
+  }
+}
+
 // Grid (B * 16 query heads, 256 / 32 dim slices); 256 threads = 32 dims x 8 chunk groups.
 // Pass 1: the largest chunk max.  Pass 2: each chunk group folds every 8th chunk's partial
 // with weight 2^(m_c - M); the 8 groups are summed through LDS.
@@ -275,6 +493,31 @@ DecodePlan decode_plan(int B, int max_keys) {
   const int chunk = max(kStep, (per + kStep - 1) / kStep * kStep);
   nchunks = max(1, (max_keys + chunk - 1) / chunk);
   return DecodePlan{nchunks, chunk};
+}
+
+hipError_t launch_decode_fp8(const bf16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                             const float* k_scale, const float* v_scale, int cap, const int* pos,
+                             int B, const bf16_t* gate, bf16_t* out, float* lse, int window,
+                             bool rope_q, const RopeTable& tab, float scale_log2e,
+                             const DecodePlan& plan, void* workspace, hipStream_t stream) {
+  const size_t parts = (size_t)B * kHkv * plan.nchunks * kGroup;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o + parts * kD;
+  const dim3 grid((unsigned)plan.nchunks, (unsigned)B);
+  if (window > 0) {
+    hipLaunchKernelGGL(decode_split_fp8_kernel<true>, grid, dim3(256), 0, stream, q, k_cache,
+                       v_cache, k_scale, v_scale, cap, pos, window, plan.chunk, plan.nchunks, ws_o,
+                       ws_ml, rope_q ? 1 : 0, tab, scale_log2e);
+  } else {
+    hipLaunchKernelGGL(decode_split_fp8_kernel<false>, grid, dim3(256), 0, stream, q, k_cache,
+                       v_cache, k_scale, v_scale, cap, pos, window, plan.chunk, plan.nchunks, ws_o,
+                       ws_ml, rope_q ? 1 : 0, tab, scale_log2e);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * kHq), kD / kCombDims), dim3(256), 0,
+                     stream, ws_o, ws_ml, plan.nchunks, gate, out, lse);
+  return hipGetLastError();
 }
 
 size_t decode_workspace_bytes(int B, const DecodePlan& plan) {

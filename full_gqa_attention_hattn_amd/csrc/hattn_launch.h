@@ -22,6 +22,12 @@ hipError_t launch_kv_append(const bf16_t* k_new, const bf16_t* v_new, bf16_t* k_
                             int window, int* slots_out, const RopeTable* rope_k,
                             hipStream_t stream);
 
+// 8-bit KV append: caches [B, cap, 4, 256] E4M3 codes, scales [B, 4, cap] fp32.
+hipError_t launch_kv_append_fp8(const bf16_t* k_new, const bf16_t* v_new, uint8_t* k_cache,
+                                uint8_t* v_cache, float* k_scale, float* v_scale, int cap,
+                                const int* pos0, int B, int n, int window, int* slots_out,
+                                const RopeTable* rope_k, hipStream_t stream);
+
 // window == 0 selects the full-causal kernel.
 hipError_t launch_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                           int cap, const int* pos0, int B, int Sq, const bf16_t* gate,
@@ -48,5 +54,13 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
                          const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
                          int window, bool rope_q, const RopeTable& tab, float scale_log2e,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+// 8-bit KV decode: caches [B, cap, 4, 256] E4M3 codes, scales [B, 4, cap] fp32; same plan
+// and workspace as launch_decode.
+hipError_t launch_decode_fp8(const bf16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                             const float* k_scale, const float* v_scale, int cap, const int* pos,
+                             int B, const bf16_t* gate, bf16_t* out, float* lse, int window,
+                             bool rope_q, const RopeTable& tab, float scale_log2e,
+                             const DecodePlan& plan, void* workspace, hipStream_t stream);
 
 }  // namespace hattn

@@ -143,6 +143,104 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   *reinterpret_cast<uint4*>(dst + half) = uint4{yb[0], yb[1], yb[2], yb[3]};
 }
 
+// 8-bit KV append: one workgroup per token.  The token's key row (rotated first when
+// rope_k) and value row are rounded to bf16 as the 16-bit cache would hold them, staged in
+// LDS, and each (row, head) of 256 values is quantized with scale = amax / 448 (fp32,
+// correctly rounded) to E4M3 codes x / scale (correctly rounded division, clamped to
+// +-448, then the hardware's round-to-nearest-even conversion).  A head's 256 values are
+// the 32 lanes x 8 values of one half-wave, so its amax is a 5-step lane reduction.
+// Caches [B, cap, 4, 256] bytes; scales [B, 4, cap] fp32.
+// [T5] §3.2 "Deployment steps and key parameters" (the 1M deployment quantizes the KV
+// cache to save memory).
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, int cap, const int* __restrict__ pos0, int n, int window,
+    int* __restrict__ slots_out, int rope_k, RopeTable tab) {
+  __shared__ f32x2 cs[kMaxHalfRot];
+  __shared__ __attribute__((aligned(16))) bf16_t row[2][kHkv * kD];
+  const long long tok = blockIdx.x;
+  const int b = (int)(tok / n), t = (int)(tok - (long long)b * n);
+  const int p = pos0[b] + t;
+  int slot;
+  bool write;
+  if (window == 0) {
+    slot = (p >= 0 && p < cap) ? p : -1;
+    write = slot >= 0;
+  } else {
+    slot = p >= 0 ? p % window : -1;
+    write = slot >= 0 && slot < cap && t >= n - window;
+  }
+  if (threadIdx.x == 0 && slots_out != nullptr) slots_out[tok] = slot;
+  if (!write) return;  // uniform over the workgroup
+  const int half = tab.rot_dim >> 1;
+  if (rope_k) {
+    for (int f = threadIdx.x; f < half; f += 256) {
+      float sv, cv;
+      sincos_angle(rope_angle(p, tab.inv_freq[f]), &sv, &cv);
+      cs[f] = f32x2{cv, sv};
+    }
+    __syncthreads();
+  }
+  const int c = threadIdx.x & 127;
+  const bool is_v = threadIdx.x >= 128;
+  const int head = c >> 5, d0 = (c & 31) * 8;
+  const bf16_t* src = (is_v ? v_new : k_new) + tok * (kHkv * kD) + c * 8;
+  bf16_t* stage = &row[is_v ? 1 : 0][c * 8];
+  // Stage the row as the 16-bit cache would hold it.
+  if (!rope_k || is_v || d0 >= 2 * half) {
+    *reinterpret_cast<uint4*>(stage) = *reinterpret_cast<const uint4*>(src);
+  } else if (d0 < half) {
+    const uint4 xa = *reinterpret_cast<const uint4*>(src);
+    const uint4 xb = *reinterpret_cast<const uint4*>(src + half);
+    const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
+    const uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
+    uint32_t ya[4], yb[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2 c0 = cs[d0 + 2 * w], c1 = cs[d0 + 2 * w + 1];
+      float ya0, yb0, ya1, yb1;
+      rope_pair(bf16_lo(wa[w]), bf16_lo(wb[w]), c0.x, c0.y, &ya0, &yb0);
+      rope_pair(bf16_hi(wa[w]), bf16_hi(wb[w]), c1.x, c1.y, &ya1, &yb1);
+      ya[w] = pack_bf16x2(ya0, ya1);
+      yb[w] = pack_bf16x2(yb0, yb1);
+    }
+    *reinterpret_cast<uint4*>(stage) = uint4{ya[0], ya[1], ya[2], ya[3]};
+    *reinterpret_cast<uint4*>(stage + half) = uint4{yb[0], yb[1], yb[2], yb[3]};
+  }
+  __syncthreads();
+  const uint4 xw = *reinterpret_cast<const uint4*>(stage);
+  const uint32_t wv[4] = {xw.x, xw.y, xw.z, xw.w};
+  float x[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    x[2 * w] = bf16_lo(wv[w]);
+    x[2 * w + 1] = bf16_hi(wv[w]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+  const float scale = __fdiv_rn(amax, kE4m3Max);
+  uint32_t codes[2] = {0u, 0u};
+  if (scale > 0.f) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = fminf(fmaxf(__fdiv_rn(x[4 * w + e], scale), -kE4m3Max), kE4m3Max);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+      codes[w] = (uint32_t)word;
+    }
+  }
+  uint8_t* dst = (is_v ? v_cache : k_cache) + ((long long)b * cap + slot) * (kHkv * kD) + c * 8;
+  *reinterpret_cast<uint2*>(dst) = uint2{codes[0], codes[1]};
+  if ((c & 31) == 0) (is_v ? v_scale : k_scale)[((long long)b * kHkv + head) * cap + slot] = scale;
+}
+
 }  // namespace
 
 hipError_t launch_rope_qk(bf16_t* q, bf16_t* k, const int* pos0, int B, int S,
@@ -162,6 +260,22 @@ hipError_t launch_kv_append(const bf16_t* k_new, const bf16_t* v_new, bf16_t* k_
   const RopeTable tab = rope_k ? *rope_k : RopeTable{};
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_new, v_new,
                      k_cache, v_cache, cap, pos0, n, window, slots_out, rope_k ? 1 : 0, tab);
+  return hipGetLastError();
+}
+
+}  // namespace hattn
+
+namespace hattn {
+
+hipError_t launch_kv_append_fp8(const bf16_t* k_new, const bf16_t* v_new, uint8_t* k_cache,
+                                uint8_t* v_cache, float* k_scale, float* v_scale, int cap,
+                                const int* pos0, int B, int n, int window, int* slots_out,
+                                const RopeTable* rope_k, hipStream_t stream) {
+  const long long grid = (long long)B * n;
+  const RopeTable tab = rope_k ? *rope_k : RopeTable{};
+  hipLaunchKernelGGL(kv_append_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, stream, k_new,
+                     v_new, k_cache, v_cache, k_scale, v_scale, cap, pos0, n, window, slots_out,
+                     rope_k ? 1 : 0, tab);
   return hipGetLastError();
 }
 

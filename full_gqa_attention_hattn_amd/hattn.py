@@ -25,10 +25,11 @@ HATTN_ERR_HIP = 7
 HATTN_SLIDING = 0
 HATTN_FULL = 1
 HATTN_ROPE_Q_FUSED = 1
+HATTN_KV8_ROPE_K = 1
 
 # Every symbol include/hattn.h declares.
 EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_kv_append_rope",
-           "hattn_prefill", "hattn_prefill_ring",
+           "hattn_prefill", "hattn_prefill_ring", "hattn_kv_append_fp8", "hattn_decode_fp8",
            "hattn_decode_workspace_bytes", "hattn_decode", "hattn_model_layer_kind",
            "hattn_model_kv_bytes", "hattn_model_decode_workspace_bytes", "hattn_model_decode",
            "hattn_model_prefill_workspace_bytes", "hattn_model_prefill",
@@ -72,6 +73,11 @@ def _load():
     lib.hattn_kv_append.restype = i32
     lib.hattn_kv_append_rope.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
     lib.hattn_kv_append_rope.restype = i32
+    lib.hattn_kv_append_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, u32, vp]
+    lib.hattn_kv_append_fp8.restype = i32
+    lib.hattn_decode_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
+                                     ctypes.c_size_t, u32, vp]
+    lib.hattn_decode_fp8.restype = i32
     iop = ctypes.POINTER(LayerIO)
     sz = ctypes.c_size_t
     lib.hattn_model_layer_kind.argtypes = [i32]
@@ -119,7 +125,11 @@ def preset(kind) -> LayerCfg:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("hattn: tensors must be contiguous (the C ABI takes dense layouts)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -217,7 +227,8 @@ def _layer_array(layers):
     for i, L in enumerate(layers):
         for name in ("q", "k", "v", "gate", "k_cache", "v_cache", "out", "lse"):
             t = L.get(name)
-            setattr(arr[i], name, None if t is None else t.data_ptr())
+            p = _ptr(t)
+            setattr(arr[i], name, None if p is None else p.value)
     return arr
 
 
@@ -245,3 +256,29 @@ def model_prefill(layers, cap: int, pos0, workspace, stream=None):
     _check(_lib.hattn_model_prefill(arr, len(layers), cap, _ptr(pos0), B, Sq, _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "hattn_model_prefill")
+
+
+# ------------------------------------------------------------------------ 8-bit KV cache --
+def kv_append_fp8(cfg: LayerCfg, k_new, v_new, k_cache, v_cache, k_scale, v_scale, pos0,
+                  slots_out=None, rope_k: bool = False, stream=None):
+    """Quantize and append into an 8-bit cache (uint8 [B,cap,4,256], scales fp32 [B,4,cap])."""
+    B, n = int(k_new.shape[0]), int(k_new.shape[1])
+    _check(_lib.hattn_kv_append_fp8(ctypes.byref(cfg), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                    int(k_cache.shape[1]), _ptr(pos0), B, n, _ptr(slots_out),
+                                    HATTN_KV8_ROPE_K if rope_k else 0, _stream(stream)),
+           "hattn_kv_append_fp8")
+
+
+def decode_fp8(cfg: LayerCfg, q, k_cache, v_cache, k_scale, v_scale, pos, gate, out, lse=None,
+               workspace=None, rope_q_fused: bool = False, stream=None):
+    B = int(q.shape[0])
+    cap = int(k_cache.shape[1])
+    if workspace is None:
+        raise ValueError("decode_fp8 needs a workspace (alloc_workspace)")
+    flags = HATTN_ROPE_Q_FUSED if rope_q_fused else 0
+    _check(_lib.hattn_decode_fp8(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_scale), _ptr(v_scale), cap, _ptr(pos), B, _ptr(gate),
+                                 _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), flags,
+                                 _stream(stream)), "hattn_decode_fp8")

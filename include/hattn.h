@@ -182,6 +182,40 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
                           const void* gate, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, uint32_t flags, void* stream);
 
+/* ---- 8-bit KV cache ------------------------------------------------------------------
+ * The library's own 8-bit cache format (for the quantized KV cache the pages' 1M
+ * deployment uses: [T5] "Why fitting a 1M context into a 4B dense model deserves its own
+ * discussion", §3.2 "Deployment steps and key parameters"):
+ *   k_cache / v_cache [B,cap,4,256] uint8 OCP FP8 E4M3 codes (sign, 4 exponent bits with
+ *     bias 7, 3 mantissa bits; 0x7F / 0xFF NaN; largest finite 448);
+ *   k_scale / v_scale [B,4,cap] fp32, one per (token, KV head) -- head-major so a head's
+ *     scales of consecutive tokens are contiguous.
+ * A stored row x (256 values of one head, the bf16 a 16-bit cache would hold) becomes
+ *   scale = fp32(amax|x| / 448),  code_d = E4M3_RNE(clamp(fp32(x_d / scale), -448, 448))
+ * (all codes 0 and scale 0 for an all-zero row); its value is code_value * scale.
+ * 2080 bytes per token per layer instead of 4096. */
+
+/* hattn_kv_append_fp8 flag: k_new is unrotated; rotate it by position first (the bits of
+ * hattn_rope_qk), then quantize.  Without it k_new must already be rotated. */
+enum { HATTN_KV8_ROPE_K = 1u };
+
+/* Quantize and append n tokens per sequence (positions pos0[b] + t) into an 8-bit cache;
+ * k_new / v_new [B,n,4,256] bf16 are only read.  Slots, ring rules, slots_out and status
+ * codes as hattn_kv_append; the scales of a written slot are overwritten with the codes. */
+hattn_status hattn_kv_append_fp8(const hattn_layer_cfg* cfg, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache, float* k_scale,
+                                 float* v_scale, int32_t cap, const int32_t* pos0, int32_t B,
+                                 int32_t n, int32_t* slots_out, uint32_t flags, void* stream);
+
+/* hattn_decode over an 8-bit cache: the attention of the dequantized keys and values (the
+ * key scale multiplies its score, the value scale its probability).  Arguments, workspace
+ * (hattn_decode_workspace_bytes), flags and errors as hattn_decode. */
+hattn_status hattn_decode_fp8(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              int32_t cap, const int32_t* pos, int32_t B, const void* gate,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              uint32_t flags, void* stream);
+
 /* ---- Whole-model driver ------------------------------------------------------------
  * The model's layers follow one schedule: layer l is full-causal iff l % 4 == 3, every
  * other layer sliding-window (36 layers: 9 full, 27 sliding).  [T1] "Hybrid attention:

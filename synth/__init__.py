@@ -134,6 +134,14 @@ WORKLOADS = {
                 "4096 queries at 1044480..1048575; full caches hold positions 0..1044479, "
                 "rings 1043968..1044479",
                 1242, dict(B=1, n_layers=36, cache_len=1044480, chunk=4096)),
+    9: Workload(9, "full_1m_decode_kv8",
+                "1M-context full layer, B=1, 8-bit KV cache (E4M3 codes, per token-head "
+                "scales) holding positions 0..1048575; one decode at 1048576",
+                1243, dict(B=1, decode_pos=1 << 20, kv_format="e4m3+fp32 scale")),
+    10: Workload(10, "full_decode_b32_p131072_kv8",
+                 "full layer, B=32, 8-bit KV cache holding positions 0..131071 per sequence; "
+                 "one decode at 131072",
+                 1244, dict(B=32, decode_pos=131072, kv_format="e4m3+fp32 scale")),
 }
 
 

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.skipif(not LIBPATH.exists(), reason="libhattn.so not bu
 
 def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(hattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hattn_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -248,3 +248,33 @@ def test_model_validation(h):
     assert pre(wsb=pneed - 16) == h.HATTN_ERR_WORKSPACE
     assert pre(ws=MIS) == h.HATTN_ERR_ALIGN
     assert pre(pos=P(0x10002)) == h.HATTN_ERR_ALIGN
+
+
+def test_fp8_validation(h):
+    lib = h.lib()
+    f, s = _cfg(h, "full"), _cfg(h, "sliding")
+    app = lambda cfg=f, **o: lib.hattn_kv_append_fp8(
+        cfg, o.get("k", A), o.get("v", A), o.get("kc", A), o.get("vc", A), o.get("ks", A),
+        o.get("vs", A), o.get("cap", 64), o.get("pos", A), o.get("B", 1), o.get("n", 4),
+        o.get("slots", None), o.get("flags", 0), None)
+    for k in ("k", "v", "kc", "vc", "ks", "vs", "pos"):
+        assert app(**{k: None}) == h.HATTN_ERR_NULL, k
+    assert app(kc=MIS) == h.HATTN_ERR_ALIGN
+    assert app(ks=P(0x10002)) == h.HATTN_ERR_ALIGN
+    assert app(flags=2) == h.HATTN_ERR_UNSUPPORTED
+    assert app(cfg=s, cap=64) == h.HATTN_ERR_RANGE
+    assert app(n=-1) == h.HATTN_ERR_SHAPE
+    assert app(n=0, k=None) == h.HATTN_OK
+    need = lib.hattn_decode_workspace_bytes(f, 2, 4096)
+    dec = lambda cfg=f, **o: lib.hattn_decode_fp8(
+        cfg, o.get("q", A), o.get("kc", A), o.get("vc", A), o.get("ks", A), o.get("vs", A),
+        o.get("cap", 4096), o.get("pos", A), o.get("B", 2), o.get("g", A), o.get("out", A),
+        None, o.get("ws", A), o.get("wsb", need), o.get("flags", 0), None)
+    for k in ("q", "kc", "vc", "ks", "vs", "pos", "g", "out"):
+        assert dec(**{k: None}) == h.HATTN_ERR_NULL, k
+    assert dec(ws=None) == h.HATTN_ERR_WORKSPACE
+    assert dec(wsb=need - 1) == h.HATTN_ERR_WORKSPACE
+    assert dec(vc=MIS) == h.HATTN_ERR_ALIGN
+    assert dec(flags=4) == h.HATTN_ERR_UNSUPPORTED
+    assert dec(cfg=s, cap=4096) == h.HATTN_ERR_RANGE
+    assert dec(B=0) == h.HATTN_OK

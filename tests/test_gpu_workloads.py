@@ -250,3 +250,49 @@ def test_model_36_layers_1m_decode(bench):
         y, lse = O.decode(_cpu(L["q"][0, 0]), kc, vc, _cpu(L["gate"][0, 0]), p, kind)
         check_outputs(_cpu(L["out"][0, 0]), _cpu(L["lse"][0, 0]), y, lse, f"w7 layer {l} ({kind})")
     _free(wl)
+
+
+def _oracle_kv8_rows(src_rows, chunk=65536):
+    """The oracle's dequantized values of a [n, 4, 256] bf16 history, quantized by the
+    oracle itself, chunk by chunk (fp32 [n, 4, 256])."""
+    outs = []
+    for r0 in range(0, src_rows.shape[0], chunk):
+        c, s = O.kv_quantize(src_rows[r0:r0 + chunk])
+        outs.append(O.kv_dequantize(c, s))
+        say(f"  oracle quantized rows {r0}..{min(r0 + chunk, src_rows.shape[0]) - 1}")
+    return torch.cat(outs)
+
+
+def _check_kv8_workload(bench, idx, seqs, sample_rows):
+    wl = bench.Kv8DecodeWorkload(idx, keep_source=True)
+    wl.step()
+    torch.cuda.synchronize()
+    P = wl.P
+    gen = torch.Generator().manual_seed(9 + idx)
+    for b in seqs:
+        src_k, src_v = _cpu(wl.source["cache_k"][b, :P]), _cpu(wl.source["cache_v"][b, :P])
+        # codes and scales of sampled rows, bit for bit
+        rows = torch.unique(torch.cat([torch.randint(0, P, (sample_rows,), generator=gen),
+                                       torch.arange(P - 64, P)]))
+        kq, ks = O.kv_quantize(src_k[rows])
+        vq, vs = O.kv_quantize(src_v[rows])
+        assert torch.equal(_cpu(wl.K[b])[rows], kq) and torch.equal(_cpu(wl.V[b])[rows], vq)
+        assert torch.equal(_cpu(wl.Ks[b]).T[rows], ks) and torch.equal(_cpu(wl.Vs[b]).T[rows], vs)
+        # the decode over the whole history, every code made by the oracle
+        _, kn = O.rope_qk(None, _cpu(wl.k[b]), P, "full")
+        kc = torch.cat([_oracle_kv8_rows(src_k), O.kv_dequantize(*O.kv_quantize(kn.to(torch.bfloat16)))])
+        vc = torch.cat([_oracle_kv8_rows(src_v), O.kv_dequantize(*O.kv_quantize(_cpu(wl.v[b])))])
+        y, lse = O.decode(_cpu(wl.q[b, 0]), kc, vc, _cpu(wl.gate[b, 0]), P, "full")
+        check_outputs(_cpu(wl.out[b, 0]), _cpu(wl.lse[b, 0]), y, lse, f"w{idx} kv8 decode b={b}")
+        del kc, vc
+    _free(wl)
+
+
+def test_kv8_decode_b32_p131072(bench):
+    say("workload 10: 8-bit KV decode, B=32 at 131072")
+    _check_kv8_workload(bench, 10, (0, 31), 4096)
+
+
+def test_kv8_decode_1m(bench):
+    say("workload 9: 8-bit KV decode at 2^20")
+    _check_kv8_workload(bench, 9, (0,), 16384)
