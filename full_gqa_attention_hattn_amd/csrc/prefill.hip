@@ -56,6 +56,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // permutation of 0..7 over r & 7.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
+// The value of lane l ^ 32 alongside lane l's own: v_permlane32_swap exchanges the two
+// half-waves of a register pair in one VALU op (no LDS round trip).  Returns {x_l, x_(l^32)}
+// in some order, which is all that a max or a sum needs.
+__device__ __forceinline__ void halves(float x, float* a, float* b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -351,7 +361,11 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       float mloc = -INFINITY;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) mloc = fmaxf(mloc, s[idx]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * sl2;
+      {
+        float a, b;
+        halves(mloc, &a, &b);
+        mloc = fmaxf(a, b) * sl2;
+      }
       // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
       // first visible key); otherwise probabilities stay below 256 and O is left alone.
       const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
@@ -423,7 +437,9 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_a, l_b;
+  halves(l_run, &l_a, &l_b);
+  const float l_tot = l_a + l_b;
   if (row_ok) {
     const long long row = (long long)b * Sq + row_i;
     const float g = bf16_to_f32(gate[row * kHq + h]);
