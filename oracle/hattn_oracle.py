@@ -374,6 +374,38 @@ def kv8_bytes_per_token_layer(n_kv_heads: int = N_KV_HEADS, head_dim: int = HEAD
     return 2 * n_kv_heads * head_dim + 2 * n_kv_heads * 4
 
 
+# --- Projections around the layer -----------------------------------------------------
+# [T1] "GQA, fused projection and output gating": one linear layer q_k_v_proj of output
+# width q_dim + 2 kv_dim replaces three projections, and its output is sliced in that
+# order into q, k and v; g_proj gives one gate score per head.  [T4] parameter table:
+# hidden_size 2560, 16 x 256 query and 4 x 256 key/value dims; its quantization section
+# names the attention output projection o_proj.  Weights use the linear-layer layout
+# [out_features, in_features]; no bias (the pages show none).
+HIDDEN = 2560
+Q_DIM = N_Q_HEADS * HEAD_DIM      # 4096
+KV_DIM = N_KV_HEADS * HEAD_DIM    # 1024
+
+
+def qkv_proj(x, w_qkv, w_g):
+    """x [T, 2560]; w_qkv [6144, 2560]; w_g [16, 2560].  Returns fp32 q [T,16,256],
+    k [T,4,256], v [T,4,256] (slices of x @ w_qkv^T in that order) and gate logits
+    [T,16] = x @ w_g^T.  fp32 products of the bf16 values."""
+    xf = x.to(torch.float32)
+    qkv = xf @ w_qkv.to(torch.float32).T
+    t = x.shape[0]
+    q = qkv[:, :Q_DIM].reshape(t, N_Q_HEADS, HEAD_DIM)
+    k = qkv[:, Q_DIM:Q_DIM + KV_DIM].reshape(t, N_KV_HEADS, HEAD_DIM)
+    v = qkv[:, Q_DIM + KV_DIM:].reshape(t, N_KV_HEADS, HEAD_DIM)
+    gate = xf @ w_g.to(torch.float32).T
+    return q, k, v, gate
+
+
+def o_proj(attn, w_o):
+    """attn [T, 16, 256] (the gated head outputs, heads concatenated) @ w_o^T with
+    w_o [2560, 4096]: [T, 2560] fp32."""
+    return attn.reshape(attn.shape[0], -1).to(torch.float32) @ w_o.to(torch.float32).T
+
+
 # --- KV memory arithmetic ([T1] "Doing the arithmetic first", "Hybrid attention") ----
 def kv_bytes_per_token_layer(n_kv_heads: int = N_KV_HEADS, head_dim: int = HEAD_DIM,
                              bytes_per_elem: int = 2) -> int:
@@ -415,6 +447,6 @@ __all__ = [
     "decode",
     "kv_bytes_per_token_layer", "kv_cache_bytes", "attention_pairs_prefill",
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "kv_quantize", "kv_dequantize", "decode_kv8",
-    "kv8_bytes_per_token_layer",
+    "kv8_bytes_per_token_layer", "HIDDEN", "Q_DIM", "KV_DIM", "qkv_proj", "o_proj",
     "sdpa_flops_per_pair",
 ]

@@ -511,6 +511,46 @@ def test_decode_kv8_is_decode_of_dequantized_cache(kind):
     assert float(rel.max()) < 0.08 and float((l8 - l).abs().max()) < 0.02
 
 
+# ------------------------------------------------------------------- projections --
+def test_qkv_slicing_with_selector_weights():
+    """Weights whose rows pick single input columns: q, k, v and the gate come out as
+    those columns, which fixes the slice order and offsets of the fused projection."""
+    T = 5
+    x = _rand((T, O.HIDDEN), 95).to(torch.bfloat16)
+    sel = torch.randint(0, O.HIDDEN, (O.Q_DIM + 2 * O.KV_DIM + 16,), generator=torch.Generator().manual_seed(94))
+    w = torch.zeros(O.Q_DIM + 2 * O.KV_DIM, O.HIDDEN, dtype=torch.bfloat16)
+    w[torch.arange(w.shape[0]), sel[:w.shape[0]]] = 1
+    wg = torch.zeros(16, O.HIDDEN, dtype=torch.bfloat16)
+    wg[torch.arange(16), sel[w.shape[0]:]] = 1
+    q, k, v, g = O.qkv_proj(x, w, wg)
+    xf = x.float()
+    assert torch.equal(q.reshape(T, -1), xf[:, sel[:O.Q_DIM]])
+    assert torch.equal(k.reshape(T, -1), xf[:, sel[O.Q_DIM:O.Q_DIM + O.KV_DIM]])
+    assert torch.equal(v.reshape(T, -1), xf[:, sel[O.Q_DIM + O.KV_DIM:w.shape[0]]])
+    assert torch.equal(g, xf[:, sel[w.shape[0]:]])
+    # head h of q is columns 256 h .. 256 h + 255 of the fused output
+    assert torch.equal(q[:, 3, 7], xf[:, sel[3 * 256 + 7]])
+
+
+def test_projections_match_library_linear_and_brute_force():
+    g = torch.Generator().manual_seed(93)
+    x = torch.randint(-3, 4, (4, O.HIDDEN), generator=g).to(torch.bfloat16)
+    w = torch.randint(-2, 3, (O.Q_DIM + 2 * O.KV_DIM, O.HIDDEN), generator=g).to(torch.bfloat16)
+    wg = torch.randint(-2, 3, (16, O.HIDDEN), generator=g).to(torch.bfloat16)
+    q, k, v, gl = O.qkv_proj(x, w, wg)
+    full = F.linear(x.double(), w.double())                     # exact: small integers
+    assert torch.equal(torch.cat([q.reshape(4, -1), k.reshape(4, -1), v.reshape(4, -1)], 1).double(), full)
+    assert torch.equal(gl.double(), F.linear(x.double(), wg.double()))
+    # o_proj against a plain loop on two outputs
+    a = torch.randint(-3, 4, (2, 16, 256), generator=g).to(torch.bfloat16)
+    wo = torch.randint(-2, 3, (O.HIDDEN, O.Q_DIM), generator=g).to(torch.bfloat16)
+    y = O.o_proj(a, wo)
+    af = a.reshape(2, -1).tolist()
+    for (t, n) in ((0, 0), (1, 2559), (1, 1234)):
+        ref = sum(af[t][i] * float(wo[n, i]) for i in range(O.Q_DIM))
+        assert float(y[t, n]) == ref
+
+
 # ------------------------------------------------------------------ closed forms --
 def test_kv_memory_matches_page_figures():
     m = json.loads((GOLD / "kv_memory.json").read_text())
