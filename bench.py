@@ -403,6 +403,44 @@ class Kv8DecodeWorkload:
                          self.out, self.lse, self.ws, rope_q_fused=True)
 
 
+class ProjWorkload:
+    """Workload 11: the fused QKV + gate projection and the output projection of one layer
+    on a 4096-token chunk, with seeded synthetic weights."""
+
+    def __init__(self, device="cuda"):
+        from full_gqa_attention_hattn_amd import hattn
+        import math
+        self.h = hattn
+        W = synth.WORKLOADS[11]
+        self.W = W
+        T, Hd = W.params["T"], W.params["hidden"]
+        self.T = T
+
+        def w(shape, s):
+            return (synth.normal_bf16(shape, s, device).float() / math.sqrt(shape[1])).to(torch.bfloat16)
+        self.w_qkv = w((6144, Hd), W.seed * 10 + 1)
+        self.w_g = w((16, Hd), W.seed * 10 + 2)
+        self.w_o = w((Hd, 4096), W.seed * 10 + 3)
+        self.x = synth.normal_bf16((T, Hd), W.seed * 10 + 4, device)
+        self.a = synth.normal_bf16((T, HQ, D), W.seed * 10 + 5, device)
+        self.q = torch.empty(T, HQ, D, dtype=torch.bfloat16, device=device)
+        self.k = torch.empty(T, HKV, D, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty_like(self.k)
+        self.g = torch.empty(T, HQ, dtype=torch.bfloat16, device=device)
+        self.y = torch.empty(T, Hd, dtype=torch.bfloat16, device=device)
+        self.stages = Stages(["qkv_proj", "o_proj"])
+        self.flop_qkv = 2 * T * Hd * (6144 + 16)
+        self.flop_o = 2 * T * 4096 * Hd
+        self.prefill_flop = 0
+        self.decode_bytes = 0
+
+    def step(self):
+        with self.stages.time("qkv_proj"):
+            self.h.qkv_proj(self.x, self.w_qkv, self.w_g, self.q, self.k, self.v, self.g)
+        with self.stages.time("o_proj"):
+            self.h.o_proj(self.a, self.w_o, self.y)
+
+
 def make_workload(idx: int, device="cuda"):
     if idx in (2, 3):
         return PrefillWorkload(idx, device)
@@ -416,6 +454,8 @@ def make_workload(idx: int, device="cuda"):
         return ModelWorkload(idx, device)
     if idx in (9, 10):
         return Kv8DecodeWorkload(idx, device)
+    if idx == 11:
+        return ProjWorkload(device)
     raise ValueError(f"no bench workload {idx} (1 is the parity-only tiny case)")
 
 
@@ -448,6 +488,17 @@ def cpu_baseline(wl, budget_s: float):
         return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                 "sample": f"prefill rows {done} of the 4096-query chunk over the full "
                           f"{wl.L0 + wl.C}-token cache, all 16 heads ({dt:.1f} s)"}
+    if isinstance(wl, ProjWorkload):
+        t0 = time.perf_counter()
+        rows, flop = 0, 0
+        x, wq, wg = wl.x.cpu(), wl.w_qkv.cpu(), wl.w_g.cpu()
+        while time.perf_counter() - t0 < min(budget_s, 10.0) and rows < wl.T:
+            O.qkv_proj(x[rows:rows + 64], wq, wg)
+            rows += 64
+        flop = 2 * rows * 2560 * (6144 + 16)
+        dt = time.perf_counter() - t0
+        return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"fused QKV + gate projection of {rows} tokens ({dt:.1f} s)"}
     if isinstance(wl, Kv8DecodeWorkload):
         t0 = time.perf_counter()
         nbytes, done = 0, 0
@@ -640,7 +691,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=list(range(2, 11)))
+    ap.add_argument("--workload", type=int, default=5, choices=list(range(2, 12)))
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -675,7 +726,18 @@ def main():
            "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16; no weights needed)"}
     stage_ms = {k: st.mean_ms(k) for k in st.t if st.t[k]}
     rec["stage_ms"] = stage_ms
-    if isinstance(wl, ModelWorkload):
+    if isinstance(wl, ProjWorkload):
+        fq, fo = wl.flop_qkv, wl.flop_o
+        rec["value"] = (fq + fo) / (ms * 1e-3) / 1e12
+        rec["unit"] = "TFLOP/s"
+        tq = fq / (stage_ms["qkv_proj"] * 1e-3) / 1e12
+        to = fo / (stage_ms["o_proj"] * 1e-3) / 1e12
+        rec["qkv_proj_TFLOPs"] = tq
+        rec["o_proj_TFLOPs"] = to
+        rec["roofline"] = {"bound": "mfma", "kernel": "proj_kernel (fused QKV + gate)",
+                           "achieved": tq, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tq / PEAK_BF16_TFLOPS, "traffic": None}
+    elif isinstance(wl, ModelWorkload):
         model_fields(rec, wl, ms, stage_ms)
     elif wl.prefill_flop:
         pf_ms = stage_ms["prefill"]

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhattn.so")
-SOURCES = ["api.hip", "rope_append.hip", "prefill.hip", "decode.hip", "model.hip"]
+SOURCES = ["api.hip", "rope_append.hip", "prefill.hip", "decode.hip", "model.hip", "proj.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -299,6 +299,33 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
       scale_log2e(cfg), plan, workspace, as_stream(stream)));
 }
 
+hattn_status hattn_qkv_proj(const void* x, int32_t T, const void* w_qkv, const void* w_gate,
+                            void* q, void* k, void* v, void* gate, void* stream) {
+  if (T < 0) return HATTN_ERR_SHAPE;
+  if (T == 0) return HATTN_OK;
+  if (!x || !w_qkv || !w_gate || !q || !k || !v || !gate) return HATTN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_gate) || !aligned16(q) ||
+      !aligned16(k) || !aligned16(v) || !aligned16(gate))
+    return HATTN_ERR_ALIGN;
+  if ((long long)T > 65535LL * 128) return HATTN_ERR_SHAPE;
+  return hip_status(hattn::launch_qkv_proj(
+      static_cast<const hattn::bf16_t*>(x), T, static_cast<const hattn::bf16_t*>(w_qkv),
+      static_cast<const hattn::bf16_t*>(w_gate), static_cast<hattn::bf16_t*>(q),
+      static_cast<hattn::bf16_t*>(k), static_cast<hattn::bf16_t*>(v),
+      static_cast<hattn::bf16_t*>(gate), as_stream(stream)));
+}
+
+hattn_status hattn_o_proj(const void* attn, int32_t T, const void* w_o, void* y, void* stream) {
+  if (T < 0) return HATTN_ERR_SHAPE;
+  if (T == 0) return HATTN_OK;
+  if (!attn || !w_o || !y) return HATTN_ERR_NULL;
+  if (!aligned16(attn) || !aligned16(w_o) || !aligned16(y)) return HATTN_ERR_ALIGN;
+  if ((long long)T > 65535LL * 128) return HATTN_ERR_SHAPE;
+  return hip_status(hattn::launch_o_proj(static_cast<const hattn::bf16_t*>(attn), T,
+                                         static_cast<const hattn::bf16_t*>(w_o),
+                                         static_cast<hattn::bf16_t*>(y), as_stream(stream)));
+}
+
 const char* hattn_status_string(hattn_status status) {
   switch (status) {
     case HATTN_OK: return "ok";

@@ -14,6 +14,7 @@ constexpr int kHkv = 4;
 constexpr int kGroup = kHq / kHkv;
 constexpr int kMaxHalfRot = 128;  // rot_dim / 2 for the widest rotary span
 constexpr float kE4m3Max = 448.f;  // largest finite E4M3 value (8-bit KV cache)
+constexpr int kProjHidden = 2560;  // model hidden size (the projections' other side)
 
 typedef uint16_t bf16_t;  // raw bf16 word
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -63,4 +63,12 @@ hipError_t launch_decode_fp8(const bf16_t* q, const uint8_t* k_cache, const uint
                              bool rope_q, const RopeTable& tab, float scale_log2e,
                              const DecodePlan& plan, void* workspace, hipStream_t stream);
 
+// Fused QKV + gate projection: x [T, 2560] @ [w_qkv; w_gate]^T written as q [T,16,256],
+// k / v [T,4,256] and gate logits [T,16]; w_qkv [6144, 2560], w_gate [16, 2560].
+hipError_t launch_qkv_proj(const bf16_t* x, int T, const bf16_t* w_qkv, const bf16_t* w_gate,
+                           bf16_t* q, bf16_t* k, bf16_t* v, bf16_t* gate, hipStream_t stream);
+// Output projection: a [T, 4096] @ w_o^T, w_o [2560, 4096] -> y [T, 2560].
+hipError_t launch_o_proj(const bf16_t* a, int T, const bf16_t* w_o, bf16_t* y,
+                         hipStream_t stream);
+
 }  // namespace hattn

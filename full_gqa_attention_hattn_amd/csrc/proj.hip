@@ -1,0 +1,168 @@
+// Projections around one attention layer on bf16 MFMA: the fused QKV + gate projection
+// (hidden 2560 -> q 4096, k 1024, v 1024, gate 16) and the output projection (4096 ->
+// 2560).  [T1] "GQA, fused projection and output gating": one linear layer whose output
+// is sliced in order into q, k and v, and a per-head g_proj gate score; [T4] parameter
+// table (hidden 2560) and its quantization section (o_proj).
+//
+// Both are Y = X W^T with X [T, K] and W [N, K] row-major (the linear-layer layout), so
+// both operands are rows with K contiguous.  A workgroup computes the 128 x 128 tile
+// Y^T[n][t] = sum_k W[n][k] X[t][k] on v_mfma_f32_32x32x16_bf16 (A = W rows, B = X rows),
+// four waves of 64 x 64.  64-wide K slices of both operands go global -> LDS directly
+// (global_load_lds_dwordx4), double-buffered, each 128-byte row with its 16-byte blocks
+// XOR-swizzled by (row >> 1) & 7 so that the 16 rows one 16-lane group reads hit 16
+// different bank groups.  The accumulator holds 4 consecutive output features of one
+// token per lane group, stored as 8-byte bf16 runs.  The fused projection's epilogue writes
+// each 128-feature tile straight into q, k, v or the gate logits (tile edges fall on the
+// slice boundaries), in the layouts the attention calls take.
+#include "hattn_device.h"
+#include "hattn_launch.h"
+
+namespace hattn {
+
+namespace {
+
+constexpr int kTile = 128;            // output features and tokens per workgroup
+constexpr int kBK = 64;               // K per stage
+constexpr int kTileBytes = kTile * kBK * 2;
+constexpr int kQDim = kHq * kD, kKvDim = kHkv * kD, kQkvDim = kQDim + 2 * kKvDim;
+constexpr int kGateRows = kHq;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void g_void;
+
+__device__ __forceinline__ int pswz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Rows row0 .. row0 + 127 (rows past `last` read row `last`), K k0 .. k0 + 63 of a
+// row-major [rows, K] matrix into LDS.  16 instructions of 1 KiB (8 rows each); wave w
+// issues 4w .. 4w + 3.  Lane l of instruction j lands at row 8j + l/8, physical block l%8,
+// so it fetches logical block (l%8) ^ pswz(row): 8 lanes read one 128-byte row segment.
+__device__ __forceinline__ void load_slice(char* dst, const bf16_t* base, long long ld, int row0,
+                                           int last, int k0, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * w + i;
+    const int row = 8 * j + (lane >> 3);
+    const int lb = (lane & 7) ^ pswz(row);
+    const long long r = min(row0 + row, last);
+    __builtin_amdgcn_global_load_lds((g_void*)(base + r * ld + k0 + 8 * lb),
+                                     (lds_void*)(dst + j * 1024), 16, 0, 0);
+  }
+}
+
+// kFused: 0 = plain Y [T, N]; 1 = the QKV + gate projection (N = 6144 + 16).
+template <int kFused>
+__global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x, int T, int K,
+                                                   const bf16_t* __restrict__ w,
+                                                   const bf16_t* __restrict__ w_gate, int N,
+                                                   bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
+                                                   bf16_t* __restrict__ y2,
+                                                   bf16_t* __restrict__ y3) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wn = wv & 1, wt = wv >> 1;
+  const int n_tile = blockIdx.x * kTile, t_tile = blockIdx.y * kTile;
+
+  // This tile's weight rows, and where its outputs go.
+  const bf16_t* wbase = w;
+  int wrow0 = n_tile, wlast = N - 1;
+  bf16_t* dst = y0;
+  int dcol0 = n_tile, dld = N, dcols = N - n_tile;
+  if (kFused) {
+    if (n_tile >= kQkvDim) {
+      wbase = w_gate; wrow0 = n_tile - kQkvDim; wlast = kGateRows - 1;
+      dst = y3; dcol0 = n_tile - kQkvDim; dld = kGateRows; dcols = kGateRows - dcol0;
+    } else {
+      wlast = kQkvDim - 1;
+      if (n_tile < kQDim) { dst = y0; dcol0 = n_tile; dld = kQDim; }
+      else if (n_tile < kQDim + kKvDim) { dst = y1; dcol0 = n_tile - kQDim; dld = kKvDim; }
+      else { dst = y2; dcol0 = n_tile - kQDim - kKvDim; dld = kKvDim; }
+      dcols = kTile;
+    }
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  const int nk = K / kBK;
+  auto load_stage = [&](int s, int kt) {
+    char* st = smem + s * 2 * kTileBytes;
+    load_slice(st, wbase, K, wrow0, wlast, kt * kBK, wv, lane);
+    load_slice(st + kTileBytes, x, K, t_tile, T - 1, kt * kBK, wv, lane);
+  };
+  load_stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  const int r32 = lane & 31, hk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_stage((kt + 1) & 1, kt + 1);
+    const char* ws = smem + (kt & 1) * 2 * kTileBytes;
+    const char* xs = ws + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int lb = 2 * kk + hk;
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int row = 64 * wn + 32 * a + r32;
+        af[a] = *reinterpret_cast<const bf16x8*>(ws + row * 128 + ((lb ^ pswz(row)) << 4));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int row = 64 * wt + 32 * b + r32;
+        bfr[b] = *reinterpret_cast<const bf16x8*>(xs + row * 128 + ((lb ^ pswz(row)) << 4));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next stage has landed
+    __syncthreads();
+  }
+
+  // acc[a][b] element 4i + j: feature 64wn + 32a + 8i + 4hk + j, token 64wt + 32b + r32.
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = t_tile + 64 * wt + 32 * b + r32;
+    if (t >= T) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 64 * wn + 32 * a + 8 * i + 4 * hk;  // column within the tile
+        if (c >= dcols) continue;
+        const uint2 v{pack_bf16x2(acc[a][b][4 * i], acc[a][b][4 * i + 1]),
+                      pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3])};
+        *reinterpret_cast<uint2*>(dst + (long long)t * dld + dcol0 + c) = v;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_proj(const bf16_t* x, int T, const bf16_t* w_qkv, const bf16_t* w_gate,
+                           bf16_t* q, bf16_t* k, bf16_t* v, bf16_t* gate, hipStream_t stream) {
+  const int N = kQkvDim + kGateRows;
+  const dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((T + kTile - 1) / kTile));
+  hipLaunchKernelGGL(proj_kernel<1>, grid, dim3(256), 0, stream, x, T, kProjHidden, w_qkv, w_gate,
+                     N, q, k, v, gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_o_proj(const bf16_t* a, int T, const bf16_t* w_o, bf16_t* y,
+                         hipStream_t stream) {
+  const dim3 grid((unsigned)(kProjHidden / kTile), (unsigned)((T + kTile - 1) / kTile));
+  hipLaunchKernelGGL(proj_kernel<0>, grid, dim3(256), 0, stream, a, T, kQDim, w_o, nullptr,
+                     kProjHidden, y, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace hattn

@@ -30,6 +30,7 @@ HATTN_KV8_ROPE_K = 1
 # Every symbol include/hattn.h declares.
 EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_kv_append_rope",
            "hattn_prefill", "hattn_prefill_ring", "hattn_kv_append_fp8", "hattn_decode_fp8",
+           "hattn_qkv_proj", "hattn_o_proj",
            "hattn_decode_workspace_bytes", "hattn_decode", "hattn_model_layer_kind",
            "hattn_model_kv_bytes", "hattn_model_decode_workspace_bytes", "hattn_model_decode",
            "hattn_model_prefill_workspace_bytes", "hattn_model_prefill",
@@ -73,6 +74,10 @@ def _load():
     lib.hattn_kv_append.restype = i32
     lib.hattn_kv_append_rope.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp]
     lib.hattn_kv_append_rope.restype = i32
+    lib.hattn_qkv_proj.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.hattn_qkv_proj.restype = i32
+    lib.hattn_o_proj.argtypes = [vp, i32, vp, vp, vp]
+    lib.hattn_o_proj.restype = i32
     lib.hattn_kv_append_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, vp, u32, vp]
     lib.hattn_kv_append_fp8.restype = i32
     lib.hattn_decode_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
@@ -282,3 +287,18 @@ def decode_fp8(cfg: LayerCfg, q, k_cache, v_cache, k_scale, v_scale, pos, gate, 
                                  _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), flags,
                                  _stream(stream)), "hattn_decode_fp8")
+
+
+# ------------------------------------------------------------------ projections --
+def qkv_proj(x, w_qkv, w_gate, q, k, v, gate, stream=None):
+    """x [T,2560] -> q [T,16,256], k/v [T,4,256], gate [T,16] (any leading batch dims that
+    flatten to T)."""
+    T = int(x.numel() // x.shape[-1])
+    _check(_lib.hattn_qkv_proj(_ptr(x), T, _ptr(w_qkv), _ptr(w_gate), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(gate), _stream(stream)), "hattn_qkv_proj")
+
+
+def o_proj(attn, w_o, y, stream=None):
+    """attn [T,16,256] -> y [T,2560]."""
+    T = int(attn.numel() // 4096)
+    _check(_lib.hattn_o_proj(_ptr(attn), T, _ptr(w_o), _ptr(y), _stream(stream)), "hattn_o_proj")

@@ -274,6 +274,24 @@ hattn_status hattn_model_prefill(const hattn_layer_io* layers, int32_t n_layers,
                                  const int32_t* pos0, int32_t B, int32_t Sq, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ---- Projections around the layer ------------------------------------------------
+ * [T1] "GQA, fused projection and output gating": one linear layer q_k_v_proj of width
+ * q_dim + 2 kv_dim whose output is sliced in that order into q, k and v, and g_proj
+ * giving one gate score per head; [T4] parameter table (hidden_size 2560) and its
+ * quantization section (o_proj).  Weights in the linear-layer layout [out, in], bf16, no
+ * bias; fp32 accumulation, outputs rounded to bf16 (nearest-even).  All device memory,
+ * 16-byte aligned; T = 0 returns HATTN_OK without looking at the pointers. */
+
+/* x [T,2560] -> q [T,16,256] (unrotated), k [T,4,256] (unrotated), v [T,4,256] and gate
+ * logits [T,16], the layouts the attention calls take; w_qkv [6144,2560] (rows 0..4095 q,
+ * 4096..5119 k, 5120..6143 v), w_gate [16,2560]. */
+hattn_status hattn_qkv_proj(const void* x, int32_t T, const void* w_qkv, const void* w_gate,
+                            void* q, void* k, void* v, void* gate, void* stream);
+
+/* attn [T,16,256] (gated head outputs, heads concatenated) -> y [T,2560] with w_o
+ * [2560,4096]. */
+hattn_status hattn_o_proj(const void* attn, int32_t T, const void* w_o, void* y, void* stream);
+
 /* Static description of a status code. */
 const char* hattn_status_string(hattn_status status);
 

@@ -142,6 +142,11 @@ WORKLOADS = {
                  "full layer, B=32, 8-bit KV cache holding positions 0..131071 per sequence; "
                  "one decode at 131072",
                  1244, dict(B=32, decode_pos=131072, kv_format="e4m3+fp32 scale")),
+    11: Workload(11, "projections_t4096",
+                 "the layer's projections on the 1M context's 4096-token chunk: fused "
+                 "QKV + gate (2560 -> 6144 + 16) and output (4096 -> 2560), seeded "
+                 "synthetic weights N(0, 1/fan_in)",
+                 1245, dict(T=4096, hidden=2560, qkv_out=6144, gate_out=16, o_in=4096)),
 }
 
 

@@ -278,3 +278,21 @@ def test_fp8_validation(h):
     assert dec(flags=4) == h.HATTN_ERR_UNSUPPORTED
     assert dec(cfg=s, cap=4096) == h.HATTN_ERR_RANGE
     assert dec(B=0) == h.HATTN_OK
+
+
+def test_projection_validation(h):
+    lib = h.lib()
+    qkv = lambda **o: lib.hattn_qkv_proj(*[o.get(k, A) for k in ("x",)], o.get("T", 8),
+                                         *[o.get(k, A) for k in ("w", "wg", "q", "k", "v", "g")], None)
+    for k in ("x", "w", "wg", "q", "k", "v", "g"):
+        assert qkv(**{k: None}) == h.HATTN_ERR_NULL, k
+        assert qkv(**{k: MIS}) == h.HATTN_ERR_ALIGN, k
+    assert qkv(T=-1) == h.HATTN_ERR_SHAPE
+    assert qkv(T=0, x=None) == h.HATTN_OK
+    assert qkv(T=65535 * 128 + 1) == h.HATTN_ERR_SHAPE
+    op = lambda **o: lib.hattn_o_proj(o.get("a", A), o.get("T", 8), o.get("w", A), o.get("y", A), None)
+    for k in ("a", "w", "y"):
+        assert op(**{k: None}) == h.HATTN_ERR_NULL, k
+        assert op(**{k: MIS}) == h.HATTN_ERR_ALIGN, k
+    assert op(T=-1) == h.HATTN_ERR_SHAPE
+    assert op(T=0, a=None) == h.HATTN_OK
