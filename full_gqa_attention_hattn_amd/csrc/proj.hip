@@ -10,7 +10,9 @@
 // four waves of 64 x 64.  64-wide K slices of both operands go global -> LDS directly
 // (global_load_lds_dwordx4), double-buffered, each 128-byte row with its 16-byte blocks
 // XOR-swizzled by (row >> 1) & 7 so that the 16 rows one 16-lane group reads hit 16
-// different bank groups.  The accumulator holds 4 consecutive output features of one
+// different bank groups.  Each MFMA of a 16-wide k-step is paired with one fragment read
+// of the next k-step.  Tiles are ordered so that each XCD works on a band of token tiles
+// across all feature tiles (L2 reuse of both operands; +16% on the 4096-token QKV case).  The accumulator holds 4 consecutive output features of one
 // token per lane group, stored as 8-byte bf16 runs.  The fused projection's epilogue writes
 // each 128-feature tile straight into q, k, v or the gate logits (tile edges fall on the
 // slice boundaries), in the layouts the attention calls take.
@@ -60,11 +62,31 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
                                                    const bf16_t* __restrict__ w_gate, int N,
                                                    bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
                                                    bf16_t* __restrict__ y2,
-                                                   bf16_t* __restrict__ y3) {
+                                                   bf16_t* __restrict__ y3, int nN, int nT) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wn = wv & 1, wt = wv >> 1;
-  const int n_tile = blockIdx.x * kTile, t_tile = blockIdx.y * kTile;
+  // Tile order: with 8+ token tiles, XCD x (blockIdx % 8) owns a contiguous band of token
+  // tiles and walks all feature tiles across it, so the workgroups resident on one XCD
+  // share their X and W slices in its L2.
+  int nb, tb;
+  {
+    const int id = (int)blockIdx.x;
+    if (nT >= 8) {
+      const int xcd = id & 7, local = id >> 3;
+      const int per = (nT + 7) >> 3;
+      const int t_lo = xcd * per;
+      const int t_cnt = max(0, min(per, nT - t_lo));
+      if (local >= nN * t_cnt) return;
+      nb = local / t_cnt;
+      tb = t_lo + local % t_cnt;
+    } else {
+      if (id >= nN * nT) return;
+      nb = id % nN;
+      tb = id / nN;
+    }
+  }
+  const int n_tile = nb * kTile, t_tile = tb * kTile;
 
   // This tile's weight rows, and where its outputs go.
   const bf16_t* wbase = w;
@@ -105,25 +127,35 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
     if (kt + 1 < nk) load_stage((kt + 1) & 1, kt + 1);
     const char* ws = smem + (kt & 1) * 2 * kTileBytes;
     const char* xs = ws + kTileBytes;
+    // Fragment f of k-step kk: f = 0, 1 are W rows (a), f = 2, 3 are X rows (b).  Each MFMA
+    // of k-step kk is paired with one read of k-step kk + 1, so reads run a k-step ahead.
+    auto frag = [&](int kk, int f) {
+      const int lb = 2 * kk + hk;
+      const int row = f < 2 ? 64 * wn + 32 * f + r32 : 64 * wt + 32 * (f - 2) + r32;
+      const char* base = f < 2 ? ws : xs;
+      return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((lb ^ pswz(row)) << 4));
+    };
+    bf16x8 cur[4], nxt[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) cur[f] = frag(0, f);
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int lb = 2 * kk + hk;
-      bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int row = 64 * wn + 32 * a + r32;
-        af[a] = *reinterpret_cast<const bf16x8*>(ws + row * 128 + ((lb ^ pswz(row)) << 4));
+      for (int j = 0; j < 4; ++j) {
+        const int a = j >> 1, b = j & 1;
+        acc[a][b] = mfma32(cur[a], cur[2 + b], acc[a][b]);
+        if (kk + 1 < kBK / 16) nxt[j] = frag(kk + 1, j);
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int row = 64 * wt + 32 * b + r32;
-        bfr[b] = *reinterpret_cast<const bf16x8*>(xs + row * 128 + ((lb ^ pswz(row)) << 4));
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+      for (int f = 0; f < 4; ++f) cur[f] = nxt[f];
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the next stage has landed
     __syncthreads();
   }
@@ -146,22 +178,27 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
   }
 }
 
+// Workgroups for nN x nT tiles: with the XCD banding, 8 bands of ceil(nT / 8) token tiles.
+long long grid_size(int nN, int nT) {
+  return nT >= 8 ? 8LL * nN * ((nT + 7) / 8) : (long long)nN * nT;
+}
+
 }  // namespace
 
 hipError_t launch_qkv_proj(const bf16_t* x, int T, const bf16_t* w_qkv, const bf16_t* w_gate,
                            bf16_t* q, bf16_t* k, bf16_t* v, bf16_t* gate, hipStream_t stream) {
   const int N = kQkvDim + kGateRows;
-  const dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((T + kTile - 1) / kTile));
-  hipLaunchKernelGGL(proj_kernel<1>, grid, dim3(256), 0, stream, x, T, kProjHidden, w_qkv, w_gate,
-                     N, q, k, v, gate);
+  const int nN = (N + kTile - 1) / kTile, nT = (T + kTile - 1) / kTile;
+  hipLaunchKernelGGL(proj_kernel<1>, dim3((unsigned)grid_size(nN, nT)), dim3(256), 0, stream, x, T,
+                     kProjHidden, w_qkv, w_gate, N, q, k, v, gate, nN, nT);
   return hipGetLastError();
 }
 
 hipError_t launch_o_proj(const bf16_t* a, int T, const bf16_t* w_o, bf16_t* y,
                          hipStream_t stream) {
-  const dim3 grid((unsigned)(kProjHidden / kTile), (unsigned)((T + kTile - 1) / kTile));
-  hipLaunchKernelGGL(proj_kernel<0>, grid, dim3(256), 0, stream, a, T, kQDim, w_o, nullptr,
-                     kProjHidden, y, nullptr, nullptr, nullptr);
+  const int nN = kProjHidden / kTile, nT = (T + kTile - 1) / kTile;
+  hipLaunchKernelGGL(proj_kernel<0>, dim3((unsigned)grid_size(nN, nT)), dim3(256), 0, stream, a, T,
+                     kQDim, w_o, nullptr, kProjHidden, y, nullptr, nullptr, nullptr, nN, nT);
   return hipGetLastError();
 }
 
