@@ -178,6 +178,89 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
   }
 }
 
+// Small T (decode steps, T <= 32): the weights dominate, so the work is split by output
+// feature and K instead.  A workgroup owns 16 features; wave w takes K quarter w and runs
+// v_mfma_f32_16x16x32_bf16 with A = 16 weight rows and B = up to 16 tokens per block, both
+// fragments loaded straight from global memory (16 bytes per lane, 4 k-steps in flight).
+// The four partial tiles are summed through LDS and wave 0 stores them.
+constexpr int kSmallRows = 16;
+constexpr int kSmallMaxT = 32;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int kFused, int kTB>
+__global__ __launch_bounds__(256) void proj_small_kernel(
+    const bf16_t* __restrict__ x, int T, int K, const bf16_t* __restrict__ w,
+    const bf16_t* __restrict__ w_gate, int N, bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
+    bf16_t* __restrict__ y2, bf16_t* __restrict__ y3) {
+  __shared__ f32x4 red[4][kTB][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * kSmallRows;
+  const bf16_t* wbase = w;
+  int wrow = n0;
+  bf16_t* dst = y0;
+  int dcol0 = n0, dld = N;
+  if (kFused) {
+    if (n0 >= kQkvDim) { wbase = w_gate; wrow = n0 - kQkvDim; dst = y3; dcol0 = n0 - kQkvDim; dld = kGateRows; }
+    else if (n0 < kQDim) { dcol0 = n0; dld = kQDim; }
+    else if (n0 < kQDim + kKvDim) { dst = y1; dcol0 = n0 - kQDim; dld = kKvDim; }
+    else { dst = y2; dcol0 = n0 - kQDim - kKvDim; dld = kKvDim; }
+  }
+  const int r16 = lane & 15, kg = lane >> 4;   // fragment row / column and k-group
+  const int kq = K / 4;                        // this wave's K range
+  const bf16_t* wr = wbase + (long long)(wrow + r16) * K + wv * kq + 8 * kg;
+  const bf16_t* xr[kTB];
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb)
+    xr[tb] = x + (long long)min(16 * tb + r16, T - 1) * K + wv * kq + 8 * kg;
+  f32x4 acc[kTB];
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) acc[tb] = f32x4{};
+  constexpr int kUnroll = 4;
+  for (int k = 0; k < kq; k += 32 * kUnroll) {
+    bf16x8 a[kUnroll], b[kUnroll][kTB];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      a[u] = *reinterpret_cast<const bf16x8*>(wr + k + 32 * u);
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) b[u][tb] = *reinterpret_cast<const bf16x8*>(xr[tb] + k + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) acc[tb] = mfma16(a[u], b[u][tb], acc[tb]);
+  }
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) red[wv][tb][lane] = acc[tb];
+  __syncthreads();
+  if (wv != 0) return;
+  // acc element j: feature n0 + 4 kg + j, token 16 tb + r16.
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) {
+    const f32x4 v = red[0][tb][lane] + red[1][tb][lane] + red[2][tb][lane] + red[3][tb][lane];
+    const int t = 16 * tb + r16;
+    if (t >= T) continue;
+    const uint2 o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<uint2*>(dst + (long long)t * dld + dcol0 + 4 * kg) = o;
+  }
+}
+
+template <int kFused>
+hipError_t launch_small(const bf16_t* x, int T, int K, const bf16_t* w, const bf16_t* w_gate,
+                        int N, bf16_t* y0, bf16_t* y1, bf16_t* y2, bf16_t* y3,
+                        hipStream_t stream) {
+  const dim3 grid((unsigned)(N / kSmallRows));
+  if (T <= 16)
+    hipLaunchKernelGGL((proj_small_kernel<kFused, 1>), grid, dim3(256), 0, stream, x, T, K, w,
+                       w_gate, N, y0, y1, y2, y3);
+  else
+    hipLaunchKernelGGL((proj_small_kernel<kFused, 2>), grid, dim3(256), 0, stream, x, T, K, w,
+                       w_gate, N, y0, y1, y2, y3);
+  return hipGetLastError();
+}
+
 // Workgroups for nN x nT tiles: with the XCD banding, 8 bands of ceil(nT / 8) token tiles.
 long long grid_size(int nN, int nT) {
   return nT >= 8 ? 8LL * nN * ((nT + 7) / 8) : (long long)nN * nT;
@@ -188,6 +271,8 @@ long long grid_size(int nN, int nT) {
 hipError_t launch_qkv_proj(const bf16_t* x, int T, const bf16_t* w_qkv, const bf16_t* w_gate,
                            bf16_t* q, bf16_t* k, bf16_t* v, bf16_t* gate, hipStream_t stream) {
   const int N = kQkvDim + kGateRows;
+  if (T <= kSmallMaxT)
+    return launch_small<1>(x, T, kProjHidden, w_qkv, w_gate, N, q, k, v, gate, stream);
   const int nN = (N + kTile - 1) / kTile, nT = (T + kTile - 1) / kTile;
   hipLaunchKernelGGL(proj_kernel<1>, dim3((unsigned)grid_size(nN, nT)), dim3(256), 0, stream, x, T,
                      kProjHidden, w_qkv, w_gate, N, q, k, v, gate, nN, nT);
@@ -196,6 +281,9 @@ hipError_t launch_qkv_proj(const bf16_t* x, int T, const bf16_t* w_qkv, const bf
 
 hipError_t launch_o_proj(const bf16_t* a, int T, const bf16_t* w_o, bf16_t* y,
                          hipStream_t stream) {
+  if (T <= kSmallMaxT)
+    return launch_small<0>(a, T, kQDim, w_o, nullptr, kProjHidden, y, nullptr, nullptr, nullptr,
+                           stream);
   const int nN = kProjHidden / kTile, nT = (T + kTile - 1) / kTile;
   hipLaunchKernelGGL(proj_kernel<0>, dim3((unsigned)grid_size(nN, nT)), dim3(256), 0, stream, a, T,
                      kQDim, w_o, nullptr, kProjHidden, y, nullptr, nullptr, nullptr, nN, nT);

@@ -49,7 +49,7 @@ def _rel_l2(gpu, ref, name, tol=2e-2):
     assert float(rel.max()) <= tol, f"{name}: rel-L2 {float(rel.max()):.3e}"
 
 
-@pytest.mark.parametrize("T", [1, 37, 300])
+@pytest.mark.parametrize("T", [1, 16, 17, 32, 37, 300])
 def test_qkv_and_o_proj_match_oracle(h, T):
     say(f"projections T={T}")
     w_qkv, w_g, w_o = _weights(181)
