@@ -15,10 +15,16 @@
 //   * S^T = K . Q^T and O^T = V^T . P^T run on v_mfma_f32_32x32x16_bf16 with fp32
 //     accumulation; a lane holds one query row's scores, so the online-softmax max needs
 //     one cross-lane exchange (lane ^ 32) and the rescale of O is lane-local;
-//   * 32-key K and V tiles go global -> LDS directly (global_load_lds_dwordx4, no staging
-//     registers), double-buffered, row-major with an XOR swizzle of the 16-byte blocks; the
-//     V^T operand is read with ds_read_b64_tr_b16, which transposes 4 keys x 16 dims per
-//     lane group, in the key order in which a lane already holds P^T in its accumulator;
+//   * 32-key K and V tiles go global -> LDS directly (the buffer form of the LDS copy, no
+//     staging registers), row-major with an XOR swizzle of the 16-byte blocks; K tiles
+//     rotate through two LDS stages and V tiles through three; the V^T operand is read
+//     with ds_read_b64_tr_b16, which transposes 4 keys x 16 dims per lane group, in the key
+//     order in which a lane already holds P^T in its accumulator;
+//   * the loop is rotated: iteration t runs the PV step of tile t - 1 first (its
+//     probabilities wait in registers), then issues the copies of tile t + 1, then QK and
+//     the softmax of tile t.  The compiler drains every pending LDS copy before a
+//     transposing read, so those reads are placed right after the barrier that waits for
+//     the copies anyway, and the issue of the next copies overlaps PV MFMAs in flight;
 //   * the row max used for exp2 only moves when a tile beats it by more than 2^8, so O is
 //     rescaled rarely (probabilities stay <= 256 in between, exact in fp32 and bf16 range);
 //   * tiles wholly outside the causal / sliding band are never visited (per workgroup, and
@@ -47,7 +53,6 @@ constexpr float kRescaleLog2 = 8.f;      // move the running max only when beate
 constexpr int kRingSlots = 512;          // sliding-layer ring: one slot per window position
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void g_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -68,6 +73,15 @@ __device__ __forceinline__ void halves(float x, float* a, float* b) {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Buffer resource for the copies of one tile (raw addressing, no stride; every offset a
+// copy uses is below 2^31, so the range check never clips).  The buffer form of the
+// global->LDS copy is counted on the vector-memory counter only, so the LDS reads that
+// follow it keep exact lgkmcnt waits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
 }
 
 // This wave's share of a 32-row tile load straight into LDS.  The tile is 16 KiB = 16
@@ -98,13 +112,14 @@ struct TileLoader {
   __device__ __forceinline__ void load(char* dst, const bf16_t* base, int row0, int last,
                                        int w) const {
     const char* tile = reinterpret_cast<const char*>(base) + (long long)row0 * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile);
     const bool tail = row0 + kBN - 1 > last;
 #pragma unroll
     for (int i = 0; i < nw; ++i) {
       const int r = tail ? min(lrow[i], last - row0) : lrow[i];
       const unsigned off = (unsigned)r * kRowBytes + (unsigned)lblk[i] * 16u;
-      __builtin_amdgcn_global_load_lds((g_void*)(tile + off),
-                                       (lds_void*)(dst + (nw * w + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (nw * w + i) * 1024), 16,
+                                               (int)off, 0, 0, 0);
     }
   }
 
@@ -115,18 +130,18 @@ struct TileLoader {
   // of copy instructions; the caller then waits for all of them.
   __device__ __forceinline__ void load_split(char* dst, const bf16_t* ring, const bf16_t* chunk,
                                              int key0, int pb, int last_row, int w) const {
-    const char* rbase = reinterpret_cast<const char*>(ring);
-    const char* cbase = reinterpret_cast<const char*>(chunk);
+    const __amdgpu_buffer_rsrc_t rr = tile_rsrc(ring);
+    const __amdgpu_buffer_rsrc_t rc = tile_rsrc(chunk);
 #pragma unroll
     for (int i = 0; i < nw; ++i) {
       const int j = key0 + lrow[i];
       lds_void* d = (lds_void*)(dst + (nw * w + i) * 1024);
       if (j < pb) {
         const unsigned off = (unsigned)(j & (kRingSlots - 1)) * kRowBytes + (unsigned)lblk[i] * 16u;
-        __builtin_amdgcn_global_load_lds((g_void*)(rbase + off), d, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, d, 16, (int)off, 0, 0, 0);
       } else {
         const unsigned off = (unsigned)min(j - pb, last_row) * kRowBytes + (unsigned)lblk[i] * 16u;
-        __builtin_amdgcn_global_load_lds((g_void*)(cbase + off), d, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, d, 16, (int)off, 0, 0, 0);
       }
     }
   }
@@ -141,7 +156,7 @@ __device__ __forceinline__ void wait_lds_dma() {
 
 // kc / vc: the position-indexed caches [B, cap, 4, 256], or in ring mode the chunk's own
 // keys / values [B, Sq, 4, 256] with the rings kr / vr [B, 512, 4, 256].
-template <bool kSliding, int kWaves, int kStages, bool kRing>
+template <bool kSliding, int kWaves, bool kRing>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
                     const bf16_t* __restrict__ vc, const bf16_t* __restrict__ kr,
@@ -156,11 +171,10 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   constexpr int kHalf = kSliding ? 128 : 32;  // rot_dim / 2
   constexpr int kNdc = kHalf / 16;           // Q fragments holding the first rotary half
   constexpr int kTile = kBN * kD * 2;        // bytes of one K or V tile
-  constexpr int kStage = 2 * kTile;
   constexpr int kPitch = kHalf + 2;          // cos/sin table row, f32x2; +16 B vs bank aliasing
   constexpr int kCsBytes = kBQ * kPitch * 8;
-  constexpr int kLdsBytes = kStages * kStage > kCsBytes ? kStages * kStage : kCsBytes;
-  constexpr int kLoadsPerTile = 2 * (16 / kWaves);  // K and V wave-instructions per wave
+  constexpr int kRingBytes = 5 * kTile;     // K tiles: 2 stages, V tiles: 3 stages
+  constexpr int kLdsBytes = kRingBytes > kCsBytes ? kRingBytes : kCsBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -276,12 +290,12 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) o[mb] = f32x16{};
   const TileLoader<kWaves> ld(w, lane);
-  // K and V tile t (key positions 32t .. 32t + 31) into LDS stage st.
-  auto load_tile = [&](char* st, int t) {
+  // K and V tile t (key positions 32t .. 32t + 31) into LDS at kd and vd.
+  auto load_tile = [&](char* kd, char* vd, int t) {
     const int key0 = t * kBN;
     if (!kRing) {
-      ld.load(st, kbase, key0, kmax, w);
-      ld.load(st + kTile, vbase, key0, kmax, w);
+      ld.load(kd, kbase, key0, kmax, w);
+      ld.load(vd, vbase, key0, kmax, w);
     } else if (key0 >= pb || key0 + kBN <= pb) {
       // One source for the whole tile: a run of the chunk's rows, or of ring slots (tiles
       // are 32-aligned, so a ring run does not wrap).  A single load() call for both keeps
@@ -289,153 +303,153 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       const bool in_ring = key0 < pb;
       const int row0 = in_ring ? (key0 & (kRingSlots - 1)) : key0 - pb;
       const int last = in_ring ? row0 + kBN - 1 : kmax - pb;
-      ld.load(st, in_ring ? krbase : kbase, row0, last, w);
-      ld.load(st + kTile, in_ring ? vrbase : vbase, row0, last, w);
+      ld.load(kd, in_ring ? krbase : kbase, row0, last, w);
+      ld.load(vd, in_ring ? vrbase : vbase, row0, last, w);
     } else {
-      ld.load_split(st, krbase, kbase, key0, pb, kmax - pb, w);
-      ld.load_split(st + kTile, vrbase, vbase, key0, pb, kmax - pb, w);
+      ld.load_split(kd, krbase, kbase, key0, pb, kmax - pb, w);
+      ld.load_split(vd, vrbase, vbase, key0, pb, kmax - pb, w);
     }
   };
   // The two waves sharing a SIMD (row blocks 0 and 1 of one head) would otherwise reach
   // their softmax phases together; issue priority for row block 0 staggers them.
   if (rb == 0) __builtin_amdgcn_s_setprio(2);
 
-  // Prologue: tiles t_lo .. t_lo + kStages - 2 in flight.
+  // K tiles rotate through two LDS stages and V tiles through three.  Iteration t first
+  // runs the PV step of tile t - 1 (its probabilities wait in registers), then issues the
+  // copies of tile t + 1, then QK and the softmax of tile t.  So the transposing V reads
+  // follow a barrier that has already drained the copies, and the issue of the next
+  // copies overlaps the PV MFMAs still in the pipe.
+  char* const kring = smem;
+  char* const vring = smem + 2 * kTile;
+  auto qk_softmax = [&](const char* kst, int t, bf16x8* pfo) __attribute__((always_inline)) {
+    // S^T[key][query]; accumulator element 4i + j of lane half hh is key 8i + 4hh + j.
+    // K fragments are read two ahead of the MFMA that consumes them.
+    auto kfrag = [&](int dc) {
+      const int blk = ((2 * dc + hh) & 7) ^ ksw;
+      return *reinterpret_cast<const bf16x8*>(kst + n * 512 + (dc >> 2) * 128 + (blk << 4));
+    };
+    f32x16 s = f32x16{};
+    bf16x8 ka = kfrag(0), kb = kfrag(1);
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i) {
-    const int t = t_lo + i;
-    if (t <= t_hi) load_tile(smem + (i % kStages) * kStage, t);
-  }
-  // (Ring mode: the tile holding the chunk start may issue more copies, so wait for all.)
-  constexpr int kAhead = kRing ? 0 : kLoadsPerTile * (kStages - 2);
-  if (t_lo + kStages - 2 <= t_hi) wait_lds_dma<kAhead>();
-  else wait_lds_dma<0>();
-  __syncthreads();
-
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const int it = t - t_lo;
-    const char* kst = smem + (it % kStages) * kStage;
-    const char* vst = kst + kTile;
-    {
-      const int tn = t + kStages - 1;  // refill the stage read during the previous tile
-      if (tn <= t_hi) load_tile(smem + ((it + kStages - 1) % kStages) * kStage, tn);
+    for (int dc = 0; dc < 16; ++dc) {
+      const bf16x8 kn = dc + 2 < 16 ? kfrag(dc + 2) : kb;
+      s = mfma32(ka, qf[dc], s);
+      ka = kb;
+      kb = kn;
     }
+    // Keep two LDS reads in flight ahead of the MFMA chain.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
-    if (t >= wt_lo && t <= wt_hi) {
-      // S^T[key][query]; accumulator element 4i + j of lane half hh is key 8i + 4hh + j.
-      // K fragments are read two ahead of the MFMA that consumes them.
-      auto kfrag = [&](int dc) {
-        const int blk = ((2 * dc + hh) & 7) ^ ksw;
-        return *reinterpret_cast<const bf16x8*>(kst + n * 512 + (dc >> 2) * 128 + (blk << 4));
-      };
-      f32x16 s = f32x16{};
-      bf16x8 ka = kfrag(0), kb = kfrag(1);
-#pragma unroll
-      for (int dc = 0; dc < 16; ++dc) {
-        const bf16x8 kn = dc + 2 < 16 ? kfrag(dc + 2) : kb;
-        s = mfma32(ka, qf[dc], s);
-        ka = kb;
-        kb = kn;
-      }
-      // Keep two LDS reads in flight ahead of the MFMA chain.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 14; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-
-      const int key0 = t * kBN;
-      const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= capk) &&
-                         (!kSliding || Pwl - key0 <= window - 1);
-      if (!whole) {
-#pragma unroll
-        for (int idx = 0; idx < 16; ++idx) {
-          const int j = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
-          const bool vis = j <= prow && j < capk && (!kSliding || prow - j <= window - 1);
-          s[idx] = vis ? s[idx] : -INFINITY;
-        }
-      }
-      // Row max of the raw scores, then scaled (sl2 > 0 commutes with max).
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int idx = 0; idx < 16; ++idx) mloc = fmaxf(mloc, s[idx]);
-      {
-        float a, b;
-        halves(mloc, &a, &b);
-        mloc = fmaxf(a, b) * sl2;
-      }
-      // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
-      // first visible key); otherwise probabilities stay below 256 and O is left alone.
-      const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
-      if (__any(bump)) {
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float rs = 0.f;
+    const int key0 = t * kBN;
+    const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= capk) &&
+                       (!kSliding || Pwl - key0 <= window - 1);
+    if (!whole) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        const float pv = fast_exp2(__builtin_fmaf(s[idx], sl2, -m_use));
-        s[idx] = pv;
-        rs += pv;
+        const int j = key0 + 8 * (idx >> 2) + 4 * hh + (idx & 3);
+        const bool vis = j <= prow && j < capk && (!kSliding || prow - j <= window - 1);
+        s[idx] = vis ? s[idx] : -INFINITY;
       }
-      l_run += rs;
-
-      // O^T += V^T P^T.  P^T of 16-key chunk c is accumulator elements 8c .. 8c+7.
-      bf16x8 pf[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const f32x4 lo = {s[8 * c], s[8 * c + 1], s[8 * c + 2], s[8 * c + 3]};
-        const f32x4 hi = {s[8 * c + 4], s[8 * c + 5], s[8 * c + 6], s[8 * c + 7]};
-        const bf16x4 pl = __builtin_convertvector(lo, bf16x4);
-        const bf16x4 ph = __builtin_convertvector(hi, bf16x4);
-        pf[c] = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
-      }
-      // V^T fragment i = 8c + mb: keys 16c + trow (slots 0..3) and 16c + 8 + trow (slots
-      // 4..7), dims 32mb + 16(g&1) + ..; read three MFMAs ahead of its use (measured: the
-      // transposing reads need more cover than the K reads, which run two ahead).
-      auto vfrag = [&](int i) {
-        const int c = i >> 3, mb = i & 7;
-        const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
-        const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
-        return __builtin_bit_cast(bf16x8,
-                                  s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-      };
-      constexpr int kVAhead = 3;
-      bf16x8 vq[kVAhead];
-#pragma unroll
-      for (int a = 0; a < kVAhead; ++a) vq[a] = vfrag(a);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bf16x8 vn = i + kVAhead < 16 ? vfrag(i + kVAhead) : vq[0];
-        o[i & 7] = mfma32(vq[0], pf[i >> 3], o[i & 7]);
-#pragma unroll
-        for (int a = 0; a + 1 < kVAhead; ++a) vq[a] = vq[a + 1];
-        vq[kVAhead - 1] = vn;
-      }
-      // Two transposing reads per fragment: 2 * kVAhead up front, then two per MFMA.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
-#pragma unroll
-      for (int i = 0; i < 16 - kVAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 1);
     }
+    // Row max of the raw scores, then scaled (sl2 > 0 commutes with max).
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) mloc = fmaxf(mloc, s[idx]);
+    {
+      float a, b;
+      halves(mloc, &a, &b);
+      mloc = fmaxf(a, b) * sl2;
+    }
+    // Move the reference max only when the tile beats it by more than 2^8 (or on a row's
+    // first visible key); otherwise probabilities stay below 256 and O is left alone.
+    const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
+    if (__any(bump)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const float p = fast_exp2(__builtin_fmaf(s[idx], sl2, -m_use));
+      s[idx] = p;
+      rs += p;
+    }
+    l_run += rs;
 
-    // Tile t + 1 must have landed before the barrier; later tiles may stay in flight.
-    if (t + kStages - 1 <= t_hi) wait_lds_dma<kAhead>();
-    else wait_lds_dma<0>();
+    // O^T += V^T P^T.  P^T of 16-key chunk c is accumulator elements 8c .. 8c+7.
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4 lo = {s[8 * c], s[8 * c + 1], s[8 * c + 2], s[8 * c + 3]};
+      const f32x4 hi = {s[8 * c + 4], s[8 * c + 5], s[8 * c + 6], s[8 * c + 7]};
+      const bf16x4 pl = __builtin_convertvector(lo, bf16x4);
+      const bf16x4 ph = __builtin_convertvector(hi, bf16x4);
+      pfo[c] = bf16x8{pl[0], pl[1], pl[2], pl[3], ph[0], ph[1], ph[2], ph[3]};
+    }
+  };
+  auto pv = [&](const char* vst, const bf16x8* pfi) __attribute__((always_inline)) {
+    // V^T fragment i = 8c + mb: keys 16c + trow (slots 0..3) and 16c + 8 + trow (slots
+    // 4..7), dims 32mb + 16(g&1) + ..; read three MFMAs ahead of its use (measured: the
+    // transposing reads need more cover than the K reads, which run two ahead).
+    auto vfrag = [&](int i) {
+      const int c = i >> 3, mb = i & 7;
+      const int blk = ((4 * mb + (tdim >> 3)) & 7) ^ tsw;
+      const int off = (16 * c + trow) * 512 + (mb >> 1) * 128 + (blk << 4) + tlo;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + off + 8 * 512));
+      return __builtin_bit_cast(bf16x8,
+                                s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+    };
+    constexpr int kVAhead = 3;
+    bf16x8 vq[kVAhead];
+#pragma unroll
+    for (int a = 0; a < kVAhead; ++a) vq[a] = vfrag(a);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8 vn = i + kVAhead < 16 ? vfrag(i + kVAhead) : vq[0];
+      o[i & 7] = mfma32(vq[0], pfi[i >> 3], o[i & 7]);
+#pragma unroll
+      for (int a = 0; a + 1 < kVAhead; ++a) vq[a] = vq[a + 1];
+      vq[kVAhead - 1] = vn;
+    }
+    // Two transposing reads per fragment: 2 * kVAhead up front, then two per MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 1);
+#pragma unroll
+    for (int i = 0; i < 16 - kVAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 1);
+  };
+
+  if (t_lo <= t_hi) load_tile(kring, vring, t_lo);
+  bf16x8 pf[2];
+  bool have_p = false;
+  int vcur = 0;  // V stage of tile t
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int it = t - t_lo;
+    // Tile t has landed for every wave, and every wave is done with iteration t - 1.
+    wait_lds_dma<0>();
     __syncthreads();
+    const int vprev = vcur == 0 ? 2 : vcur - 1;
+    const int vnext = vcur == 2 ? 0 : vcur + 1;
+    if (have_p) pv(vring + vprev * kTile, pf);
+    if (t + 1 <= t_hi) load_tile(kring + ((it + 1) & 1) * kTile, vring + vnext * kTile, t + 1);
+    have_p = t >= wt_lo && t <= wt_hi;
+    if (have_p) qk_softmax(kring + (it & 1) * kTile, t, pf);
+    vcur = vnext;
   }
+  if (have_p) pv(vring + (vcur == 0 ? 2 : vcur - 1) * kTile, pf);
 
   float l_a, l_b;
   halves(l_run, &l_a, &l_b);
@@ -467,7 +481,6 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 // see a 512-key band, where 32-row blocks waste fewer keys at the band edges.
 constexpr int kWavesFull = 8;
 constexpr int kWavesSliding = 4;
-constexpr int kStagesSel = 2;  // K/V tiles resident in LDS
 
 template <bool kSliding, int kWaves, bool kRing>
 hipError_t launch_kind(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
@@ -479,7 +492,7 @@ hipError_t launch_kind(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_c
   const long long nwork = (long long)B * kHkv * nqb;
   // Sliding grids are padded to a multiple of 8 for the XCD-contiguous mapping.
   const long long grid = kSliding ? (nwork + 7) / 8 * 8 : nwork;
-  hipLaunchKernelGGL((prefill_kernel<kSliding, kWaves, kStagesSel, kRing>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((prefill_kernel<kSliding, kWaves, kRing>), dim3((unsigned)grid),
                      dim3(64 * kWaves), 0, stream, q, k_cache, v_cache, k_ring, v_ring, cap, pos0,
                      B, Sq, gate, out, lse, window, rope_q ? 1 : 0, tab, scale_log2e, nqb,
                      (int)nwork);
