@@ -47,45 +47,43 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) { return __builtin_bit_ca
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// sin and cos of an fp32 angle, accurate to well below one fp32 ulp for |x| < 2^30.
-// Range reduction: Cody and Waite's additive reduction by pi/2 with a two-word pi/2 in
-// double precision and fused multiply-adds (k * C1 is exact inside the fma, the residual
-// C2 = pi/2 - C1 carries the next 53 bits).  Kernels: Taylor-Maclaurin series of sin and
-// cos on |r| <= pi/4, truncated where the next term is below 1e-11.
-__device__ __forceinline__ void sincos_angle(float xf, float* s_out, float* c_out) {
-  const double x = (double)xf;
-  const double kTwoOverPi = 0.63661977236758134308;
-  const double kC1 = 1.5707963267948965580e+00;  // pi/2 rounded to double
-  const double kC2 = 6.1232339957367658e-17;     // pi/2 - kC1
-  const double k = __builtin_rint(x * kTwoOverPi);
-  double r = __builtin_fma(-k, kC1, x);
-  r = __builtin_fma(-k, kC2, r);
-  const double r2 = r * r;
-  // sin r = r (1 - r^2/3! + r^4/5! - r^6/7! + r^8/9! - r^10/11!)
-  double sp = -2.5052108385441718775e-08;         // -1/11!
-  sp = __builtin_fma(sp, r2, 2.7557319223985890653e-06);   // 1/9!
-  sp = __builtin_fma(sp, r2, -1.9841269841269841270e-04);  // -1/7!
-  sp = __builtin_fma(sp, r2, 8.3333333333333333333e-03);   // 1/5!
-  sp = __builtin_fma(sp, r2, -1.6666666666666666667e-01);  // -1/3!
-  const double sn = __builtin_fma(sp * r2, r, r);
-  // cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10! + r^12/12!
-  double cp = 2.0876756987868098979e-09;          // 1/12!
-  cp = __builtin_fma(cp, r2, -2.7557319223985890653e-07);  // -1/10!
-  cp = __builtin_fma(cp, r2, 2.4801587301587301587e-05);   // 1/8!
-  cp = __builtin_fma(cp, r2, -1.3888888888888888889e-03);  // -1/6!
-  cp = __builtin_fma(cp, r2, 4.1666666666666666667e-02);   // 1/4!
-  cp = __builtin_fma(cp, r2, -0.5);
-  const double cs = __builtin_fma(cp, r2, 1.0);
-  const int q = (int)((long long)k & 3);
-  double s, c;
+// sin and cos of an fp32 angle, with an absolute error below 1e-7 for 0 <= x < 2^21 (checked
+// against fp64 sin and cos over every RoPE angle p * omega_i with p < 2^20 + 4096: 7.4e-8).
+// Range reduction: Cody and Waite's additive reduction by pi/2, in fp32 with a three-part
+// constant: C1 = fp32(pi/2), C2 = fp32(pi/2 - C1), C3 = -2^-49 the next piece.  Each product
+// k * Ci is exact inside its fma, and x - k * C1 is exact (a multiple of 2^-23 below 1 in
+// magnitude).  k = rint(x * 2/pi) rounded in fp32 can miss the nearest quadrant by a little,
+// so |r| <= 0.88; there the Taylor-Maclaurin series of sin to r^9 and of cos to r^10 are
+// truncated below 6e-9.
+__device__ __forceinline__ void sincos_angle(float x, float* s_out, float* c_out) {
+  const float k = __builtin_rintf(__fmul_rn(x, 0.636619772f));  // 2/pi
+  float r = __builtin_fmaf(-k, 1.57079637f, x);                   // C1
+  r = __builtin_fmaf(-k, -4.37113883e-08f, r);                    // C2
+  r = __builtin_fmaf(-k, -1.77635684e-15f, r);                    // C3
+  const float r2 = r * r;
+  // sin r = r (1 - r^2/3! + r^4/5! - r^6/7! + r^8/9!)
+  float sp = 2.75573192e-06f;                        // 1/9!
+  sp = __builtin_fmaf(sp, r2, -1.98412698e-04f);     // -1/7!
+  sp = __builtin_fmaf(sp, r2, 8.33333333e-03f);      // 1/5!
+  sp = __builtin_fmaf(sp, r2, -1.66666667e-01f);     // -1/3!
+  const float sn = __builtin_fmaf(sp * r2, r, r);
+  // cos r = 1 - r^2/2! + r^4/4! - r^6/6! + r^8/8! - r^10/10!
+  float cp = -2.75573192e-07f;                       // -1/10!
+  cp = __builtin_fmaf(cp, r2, 2.48015873e-05f);      // 1/8!
+  cp = __builtin_fmaf(cp, r2, -1.38888889e-03f);     // -1/6!
+  cp = __builtin_fmaf(cp, r2, 4.16666667e-02f);      // 1/4!
+  cp = __builtin_fmaf(cp, r2, -0.5f);
+  const float cs = __builtin_fmaf(cp, r2, 1.0f);
+  const int q = (int)k & 3;
+  float s, c;
   switch (q) {
     case 0: s = sn; c = cs; break;
     case 1: s = cs; c = -sn; break;
     case 2: s = -sn; c = -cs; break;
     default: s = -cs; c = sn; break;
   }
-  *s_out = (float)s;
-  *c_out = (float)c;
+  *s_out = s;
+  *c_out = c;
 }
 
 // RoPE angle of frequency index i at position p: one fp32 multiply, rounded to nearest.
