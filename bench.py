@@ -8,9 +8,12 @@ split-KV partials and their log-sum-exp combine).
 
 Default workload (the 1M-context full layer, B=1): a cache holding positions
 0..1044479, a chunked prefill of 4096 queries at positions 1044480..1048575, then one
-decode at position 1048576 over 1048577 keys.  Other workloads (--workload 2|3|4|6) are
-the 32K sliding prefill, the 128K full prefill, the B=32 mixed decode at 128K and the
-sliding-layer side of the 1M chunk (prefill against the 512-slot ring, append, decode).
+decode at position 1048576 over 1048577 keys.  Other workloads (--workload 2..11):
+2 the 32K sliding prefill, 3 the 128K full prefill, 4 the B=32 mixed decode at 128K,
+6 the sliding-layer side of the 1M chunk (prefill against the 512-slot ring, append,
+decode), 7 and 8 the 36-layer decode step and chunk prefill at 1M, 9 and 10 the decode
+over the 8-bit KV cache at 1M and at B=32 x 128K, 11 the fused QKV + gate and output
+projections on a 4096-token chunk.
 
 Prints one JSON line.  `value` is the prefill attention throughput of the whole step
 (algorithmic prefill FLOP / step time); the decode KV bandwidth and per-kernel rates,
