@@ -12,8 +12,10 @@
 // Per 32-key step a wave computes S^T = K . Q^T for its 4 query heads on
 // v_mfma_f32_16x16x32_bf16 (K rows feed the MFMA straight from global memory; columns
 // 4..15 of Q^T are zero), runs the online softmax, and accumulates P.V on the VALU with the
-// probabilities broadcast through LDS.  It writes a partial (max, sum, o[4][256]) per
-// (b, kv head, chunk).
+// probabilities broadcast through LDS: two keys at a time with v_dot2_f32_bf16 (the same
+// dim of both keys permuted into one bf16 pair, the probabilities rounded to bf16).  The
+// reference max moves only when a step beats it by more than 2^8, so O is rarely
+// rescaled.  It writes a partial (reference max, sum, o[4][256]) per (b, kv head, chunk).
 // Phase 2 (decode_combine_kernel): per (b, query head, 32-dim slice), merges the chunk
 // partials by log-sum-exp, applies 1/l and the sigmoid gate, stores bf16 (and the LSE).
 #include "hattn_device.h"
@@ -24,6 +26,7 @@ namespace hattn {
 namespace {
 
 constexpr int kStep = 32;  // keys per wave step
+constexpr float kRescaleLog2 = 8.f;  // move the reference max only when beaten by 2^8
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -135,9 +138,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // The reference max moves only when a step beats it by more than 2^8 (or on the first
+    // visible key): probabilities stay below 256, and O is rescaled on those steps only.
+    const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
+    if (__any(bump)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      // Per-head factors live in lanes 0..3 (column = head, k-group 0).
+      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+      const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
+      const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
+      const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[0][e] *= a0;
+        o[1][e] *= a1;
+        o[2][e] *= a2;
+        o[3][e] *= a3;
+      }
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rsum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -147,8 +169,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         s[blk][j] = pj;
         rsum += pj;
       }
-    l_run = l_run * alpha + rsum;
-    m_run = m_new;
+    l_run += rsum;
 
     if (qlane) {
 #pragma unroll
@@ -156,30 +177,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) p_lds[kvh][16 * blk + 4 * g + j][n16] = s[blk][j];
     }
-    // Per-head rescale factors live in lanes 0..3 (column = head, k-group 0).
-    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
-    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
-    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[0][e] *= a0;
-      o[1][e] *= a1;
-      o[2][e] *= a2;
-      o[3][e] *= a3;
-    }
     wave_lds_fence();
+    // Keys a = 2kp + half and b = a + 2 share a lane: one permute gathers the same dim of
+    // both into a bf16 pair, and one dot2 adds p_a v_a + p_b v_b (probabilities in bf16).
 #pragma unroll
-    for (int kp = 0; kp < 16; ++kp) {
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(&p_lds[kvh][2 * kp + half][0]);
-      const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vv[kp]);
+    for (int kp = 0; kp < 16; kp += 2) {
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(&p_lds[kvh][2 * kp + half][0]);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(&p_lds[kvh][2 * kp + 2 + half][0]);
+      bf16x2 pp[kGroup];
+#pragma unroll
+      for (int hl = 0; hl < kGroup; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
+      const uint32_t* va = reinterpret_cast<const uint32_t*>(&vv[kp]);
+      const uint32_t* vb2 = reinterpret_cast<const uint32_t*>(&vv[kp + 1]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float v0 = bf16_lo(vw[w]), v1 = bf16_hi(vw[w]);
+        const bf16x2 d0 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x05040100u));
+        const bf16x2 d1 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x07060302u));
 #pragma unroll
         for (int hl = 0; hl < kGroup; ++hl) {
-          o[hl][2 * w] += pv[hl] * v0;
-          o[hl][2 * w + 1] += pv[hl] * v1;
+          o[hl][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(d0, pp[hl], o[hl][2 * w], false);
+          o[hl][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(d1, pp[hl], o[hl][2 * w + 1], false);
         }
       }
     }
@@ -346,9 +363,28 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
     load_k(kn);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // The reference max moves only when a step beats it by more than 2^8 (or on the first
+    // visible key): probabilities stay below 256, and O is rescaled on those steps only.
+    const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
+    if (__any(bump)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      // Per-head factors live in lanes 0..3 (column = head, k-group 0).
+      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+      const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
+      const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
+      const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        o[0][e] *= a0;
+        o[1][e] *= a1;
+        o[2][e] *= a2;
+        o[3][e] *= a3;
+      }
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rsum = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -358,8 +394,7 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
         sv[blk][j] = pj;
         rsum += pj;
       }
-    l_run = l_run * alpha + rsum;
-    m_run = m_new;
+    l_run += rsum;
 
     if (qlane) {
 #pragma unroll
@@ -368,31 +403,32 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
         for (int j = 0; j < 4; ++j)
           p_lds[kvh][16 * blk + 4 * g + j][n16] = sv[blk][j] * vsc[blk][j];
     }
-    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
-    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
-    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      o[0][e] *= a0;
-      o[1][e] *= a1;
-      o[2][e] *= a2;
-      o[3][e] *= a3;
-    }
     wave_lds_fence();
+    // Keys a = kq + 8j and b = a + 4 share a lane: a byte permute interleaves their codes,
+    // one conversion yields the (a, b) pair of a dim in bf16, and one dot2 adds p_a v_a +
+    // p_b v_b (probabilities, with the V scales folded in, in bf16).
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(&p_lds[kvh][kq + 4 * i][0]);
-      const uint32_t vw[4] = {vraw[i].x, vraw[i].y, vraw[i].z, vraw[i].w};
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(&p_lds[kvh][kq + 8 * j][0]);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(&p_lds[kvh][kq + 8 * j + 4][0]);
+      bf16x2 pp[kGroup];
+#pragma unroll
+      for (int hl = 0; hl < kGroup; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
+      const uint32_t va[4] = {vraw[2 * j].x, vraw[2 * j].y, vraw[2 * j].z, vraw[2 * j].w};
+      const uint32_t vb2[4] = {vraw[2 * j + 1].x, vraw[2 * j + 1].y, vraw[2 * j + 1].z, vraw[2 * j + 1].w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[w], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[w], true);
-        const float v4[4] = {lo[0], lo[1], hi[0], hi[1]};
+        const uint32_t lo = __builtin_amdgcn_perm(vb2[w], va[w], 0x05010400u);  // a0 b0 a1 b1
+        const uint32_t hi = __builtin_amdgcn_perm(vb2[w], va[w], 0x07030602u);  // a2 b2 a3 b3
+        const bf16x2 d[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false),
+                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true),
+                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false),
+                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int hl = 0; hl < kGroup; ++hl) o[hl][4 * w + e] += pv[hl] * v4[e];
+          for (int hl = 0; hl < kGroup; ++hl)
+            o[hl][4 * w + e] = __builtin_amdgcn_fdot2_f32_bf16(d[e], pp[hl], o[hl][4 * w + e], false);
       }
     }
     load_v(kn);
