@@ -55,15 +55,6 @@ hattn_status check_cfg(const hattn_layer_cfg* cfg) {
   return HATTN_OK;
 }
 
-hattn::RopeTable rope_table(const hattn_layer_cfg* cfg) {
-  hattn::RopeTable t{};
-  t.rot_dim = cfg->rot_dim;
-  for (int i = 0; i < cfg->rot_dim / 2; ++i)
-    t.inv_freq[i] = (float)std::pow(cfg->rope_theta, -2.0 * i / (double)cfg->rot_dim);
-  return t;
-}
-
-float scale_log2e(const hattn_layer_cfg* cfg) { return cfg->softmax_scale * kLog2e; }
 
 hattn_status hip_status(hipError_t e) {
   if (e == hipSuccess) return HATTN_OK;
@@ -78,6 +69,21 @@ int decode_max_keys(const hattn_layer_cfg* cfg, int32_t cap) {
 }
 
 }  // namespace
+
+namespace hattn {
+RopeTable rope_table(const ::hattn_layer_cfg* cfg) {
+  RopeTable t{};
+  t.rot_dim = cfg->rot_dim;
+  for (int i = 0; i < cfg->rot_dim / 2; ++i)
+    t.inv_freq[i] = (float)std::pow(cfg->rope_theta, -2.0 * i / (double)cfg->rot_dim);
+  return t;
+}
+
+float scale_log2e(const ::hattn_layer_cfg* cfg) { return cfg->softmax_scale * kLog2e; }
+}  // namespace hattn
+
+using hattn::rope_table;
+using hattn::scale_log2e;
 
 int32_t hattn::note_hip_error(hipError_t e) { return hip_status(e == hipSuccess ? hipErrorUnknown : e); }
 

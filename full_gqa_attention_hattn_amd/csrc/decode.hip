@@ -39,6 +39,141 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
+// Operands of one 32-key step of a wave: K rows (MFMA view) and V rows (PV view).
+struct StepRegs {
+  bf16x8 kf[2][8];
+  uint4 vv[16];
+};
+
+// Issue this lane's loads of the step at keys k0 .. k0 + 31 (of [.., k_end)) of the KV
+// head whose cache rows (4 heads x 256 dims) start at kb / vb.
+__device__ __forceinline__ void load_step(StepRegs& r, const bf16_t* kb, const bf16_t* vb, int k0,
+                                          int k_end, int lane) {
+  constexpr long long rs = kHkv * kD;
+  const int n16 = lane & 15, g = lane >> 4;    // MFMA view: column (head) and k-group
+  const int half = lane >> 5, dg = lane & 31;  // PV view: key parity and 8-dim group
+  // Keys past k_end read row k_end - 1 instead (their scores are masked to -inf, so those
+  // values meet a zero probability): unconditional loads the compiler can count, so the
+  // QK chain waits only for K while V is still in flight.
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int key = min(k0 + 16 * blk + n16, k_end - 1);
+    const bf16_t* kr = kb + (long long)key * rs + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) r.kf[blk][dc] = *reinterpret_cast<const bf16x8*>(kr + 32 * dc);
+  }
+#pragma unroll
+  for (int kp = 0; kp < 16; ++kp) {
+    const int key = min(k0 + 2 * kp + half, k_end - 1);
+    r.vv[kp] = *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 8 * dg);
+  }
+}
+
+// One 32-key step on loaded operands: S^T = K . Q^T on MFMA, the online softmax and P.V on
+// the VALU, the probabilities going through this wave's slice `pl` of LDS.
+__device__ __forceinline__ void compute_step(const StepRegs& r, const bf16x8 (&qf)[8], int k0,
+                                             int k_end, float sl2, float (*pl)[4], int lane,
+                                             float& m_run, float& l_run, float (&o)[kGroup][8]) {
+  const int n16 = lane & 15, g = lane >> 4;
+  const int half = lane >> 5;
+  const bool qlane = n16 < kGroup;
+  f32x4 s[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+  for (int dc = 0; dc < 8; ++dc) {
+    s[0] = mfma16(r.kf[0][dc], qf[dc], s[0]);
+    s[1] = mfma16(r.kf[1][dc], qf[dc], s[1]);
+  }
+  // s[blk][j] = score of key k0 + 16 blk + 4g + j for head column n16.
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = k0 + 16 * blk + 4 * g + j;
+      const float v = key < k_end ? s[blk][j] * sl2 : -INFINITY;
+      s[blk][j] = v;
+      mloc = fmaxf(mloc, v);
+    }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  // The reference max moves only when a step beats it by more than 2^8 (or on the first
+  // visible key): probabilities stay below 256, and O is rescaled on those steps only.
+  const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
+  if (__any(bump)) {
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+    // Per-head factors live in lanes 0..3 (column = head, k-group 0).
+    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
+    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
+    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[0][e] *= a0;
+      o[1][e] *= a1;
+      o[2][e] *= a2;
+      o[3][e] *= a3;
+    }
+  }
+  const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  float rsum = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pj = fast_exp2(s[blk][j] - m_use);
+      s[blk][j] = pj;
+      rsum += pj;
+    }
+  l_run += rsum;
+
+  if (qlane) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pl[16 * blk + 4 * g + j][n16] = s[blk][j];
+  }
+  wave_lds_fence();
+  // Keys a = 2kp + half and b = a + 2 share a lane: one permute gathers the same dim of
+  // both into a bf16 pair, and one dot2 adds p_a v_a + p_b v_b (probabilities in bf16).
+#pragma unroll
+  for (int kp = 0; kp < 16; kp += 2) {
+    const f32x4 pa = *reinterpret_cast<const f32x4*>(&pl[2 * kp + half][0]);
+    const f32x4 pb = *reinterpret_cast<const f32x4*>(&pl[2 * kp + 2 + half][0]);
+    bf16x2 pp[kGroup];
+#pragma unroll
+    for (int hl = 0; hl < kGroup; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
+    const uint32_t* va = reinterpret_cast<const uint32_t*>(&r.vv[kp]);
+    const uint32_t* vb2 = reinterpret_cast<const uint32_t*>(&r.vv[kp + 1]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 d0 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x05040100u));
+      const bf16x2 d1 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x07060302u));
+#pragma unroll
+      for (int hl = 0; hl < kGroup; ++hl) {
+        o[hl][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(d0, pp[hl], o[hl][2 * w], false);
+        o[hl][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(d1, pp[hl], o[hl][2 * w + 1], false);
+      }
+    }
+  }
+  wave_lds_fence();
+}
+
+// One wave's pass over keys [k_begin, k_end) of its KV head, one 32-key step at a time.
+// Leaves this lane's share of the partial (reference max, sum, o[head][8 dims]).
+__device__ __forceinline__ void attend_keys(const bf16x8 (&qf)[8], const bf16_t* kb,
+                                            const bf16_t* vb, int k_begin, int k_end, float sl2,
+                                            float (*pl)[4], int lane, float& m_run, float& l_run,
+                                            float (&o)[kGroup][8]) {
+  for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
+    StepRegs r;
+    load_step(r, kb, vb, k0, k_end, lane);
+    compute_step(r, qf, k0, k_end, sl2, pl, lane, m_run, l_run, o);
+  }
+}
+
 template <bool kSliding>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
@@ -88,7 +223,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
   }
 
-  constexpr long long rs = kHkv * kD;
   const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
   const bf16_t* kb = kc + kv_off;
   const bf16_t* vb = vc + kv_off;
@@ -100,108 +234,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
 
-  for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
-    // Keys past k_end read row k_end - 1 instead (their scores are masked to -inf, so those
-    // values meet a zero probability): unconditional loads the compiler can count, so the
-    // QK chain waits only for K while V is still in flight.
-    bf16x8 kf[2][8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int key = min(k0 + 16 * blk + n16, k_end - 1);
-      const bf16_t* kr = kb + (long long)key * rs + 8 * g;
-#pragma unroll
-      for (int dc = 0; dc < 8; ++dc) kf[blk][dc] = *reinterpret_cast<const bf16x8*>(kr + 32 * dc);
-    }
-    uint4 vv[16];
-#pragma unroll
-    for (int kp = 0; kp < 16; ++kp) {
-      const int key = min(k0 + 2 * kp + half, k_end - 1);
-      vv[kp] = *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 8 * dg);
-    }
-
-    f32x4 s[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc) {
-      s[0] = mfma16(kf[0][dc], qf[dc], s[0]);
-      s[1] = mfma16(kf[1][dc], qf[dc], s[1]);
-    }
-    // s[blk][j] = score of key k0 + 16 blk + 4g + j for head column n16.
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 16 * blk + 4 * g + j;
-        const float v = key < k_end ? s[blk][j] * sl2 : -INFINITY;
-        s[blk][j] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // The reference max moves only when a step beats it by more than 2^8 (or on the first
-    // visible key): probabilities stay below 256, and O is rescaled on those steps only.
-    const bool bump = mloc > m_run + kRescaleLog2 || (m_run == -INFINITY && mloc != -INFINITY);
-    if (__any(bump)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-      // Per-head factors live in lanes 0..3 (column = head, k-group 0).
-      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-      const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
-      const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
-      const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[0][e] *= a0;
-        o[1][e] *= a1;
-        o[2][e] *= a2;
-        o[3][e] *= a3;
-      }
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float rsum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pj = fast_exp2(s[blk][j] - m_use);
-        s[blk][j] = pj;
-        rsum += pj;
-      }
-    l_run += rsum;
-
-    if (qlane) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p_lds[kvh][16 * blk + 4 * g + j][n16] = s[blk][j];
-    }
-    wave_lds_fence();
-    // Keys a = 2kp + half and b = a + 2 share a lane: one permute gathers the same dim of
-    // both into a bf16 pair, and one dot2 adds p_a v_a + p_b v_b (probabilities in bf16).
-#pragma unroll
-    for (int kp = 0; kp < 16; kp += 2) {
-      const f32x4 pa = *reinterpret_cast<const f32x4*>(&p_lds[kvh][2 * kp + half][0]);
-      const f32x4 pb = *reinterpret_cast<const f32x4*>(&p_lds[kvh][2 * kp + 2 + half][0]);
-      bf16x2 pp[kGroup];
-#pragma unroll
-      for (int hl = 0; hl < kGroup; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
-      const uint32_t* va = reinterpret_cast<const uint32_t*>(&vv[kp]);
-      const uint32_t* vb2 = reinterpret_cast<const uint32_t*>(&vv[kp + 1]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const bf16x2 d0 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x05040100u));
-        const bf16x2 d1 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x07060302u));
-#pragma unroll
-        for (int hl = 0; hl < kGroup; ++hl) {
-          o[hl][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(d0, pp[hl], o[hl][2 * w], false);
-          o[hl][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(d1, pp[hl], o[hl][2 * w + 1], false);
-        }
-      }
-    }
-    wave_lds_fence();
-  }
+  attend_keys(qf, kb, vb, k_begin, k_end, sl2, p_lds[kvh], lane, m_run, l_run, o);
 
   // Fold the two key parities together, then the softmax sums over the 4 k-groups.
 #pragma unroll
@@ -516,6 +549,159 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
 }
 
+constexpr int kRingWaves = 4;  // waves of the fused ring step
+
+// One decode step of a sliding layer in a single launch: append, attention over the ring
+// and the merge.  Workgroup (kv head, b) rotates the new key by the token's position p and
+// writes K and V to ring slot p mod 512 (the same bits as the rotating append), then
+// attends query heads 4 kvh .. 4 kvh + 3 over the ring's min(p + 1, 512) filled slots: each
+// of the 4 waves takes 128 slots (four of the split kernel's steps), and the 4 partials are
+// merged by log-sum-exp through LDS, normalised, gated and stored as the combine does.
+// The cos/sin of p * omega_i are computed once and serve both the key and the query.
+// [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
+// tokens); [T3] "Sliding window 512" (RoPE theta 1e4 over all 256 dims).
+__global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
+    const bf16_t* __restrict__ v_new, bf16_t* __restrict__ k_ring, bf16_t* __restrict__ v_ring,
+    const int* __restrict__ pos, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
+    float* __restrict__ lse, RopeTable tab, float sl2) {
+  constexpr int kSlots = 512;
+  constexpr int kHalf = 128;       // rot_dim / 2
+  constexpr int kPerWave = kSlots / kRingWaves;
+  __shared__ f32x2 cs[kHalf];
+  __shared__ __attribute__((aligned(16))) float p_lds[kRingWaves][kStep][4];
+  __shared__ __attribute__((aligned(16))) float part_o[kRingWaves][kGroup][kD];
+  __shared__ float part_ml[kRingWaves][kGroup][2];
+
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int half = lane >> 5, dg = lane & 31;
+  const int p = pos[b];
+
+  // The query's loads go out first; the append and its fence hide their latency.
+  const bool qlane = n16 < kGroup;
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = q + ((long long)b * kHq + kvh * kGroup + (qlane ? n16 : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+  }
+
+  if (tid < kHalf) {
+    float sv, cv;
+    sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
+    cs[tid] = f32x2{cv, sv};
+  }
+  __syncthreads();
+
+  const long long ring_off = ((long long)b * kSlots * kHkv + kvh) * kD;
+  if (p >= 0) {
+    const long long row = ring_off + (long long)(p & (kSlots - 1)) * kHkv * kD;
+    const long long src = ((long long)b * kHkv + kvh) * kD;
+    if (tid < kHalf / 8) {
+      // Dims d0 .. d0 + 7 and their partners d0 + 128 .. d0 + 135.
+      const int d0 = 8 * tid;
+      const uint4 xa = *reinterpret_cast<const uint4*>(k_new + src + d0);
+      const uint4 xb = *reinterpret_cast<const uint4*>(k_new + src + d0 + kHalf);
+      const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
+      const uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
+      uint32_t ya[4], yb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 c0 = cs[d0 + 2 * e], c1 = cs[d0 + 2 * e + 1];
+        float ya0, yb0, ya1, yb1;
+        rope_pair(bf16_lo(wa[e]), bf16_lo(wb[e]), c0.x, c0.y, &ya0, &yb0);
+        rope_pair(bf16_hi(wa[e]), bf16_hi(wb[e]), c1.x, c1.y, &ya1, &yb1);
+        ya[e] = pack_bf16x2(ya0, ya1);
+        yb[e] = pack_bf16x2(yb0, yb1);
+      }
+      *reinterpret_cast<uint4*>(k_ring + row + d0) = uint4{ya[0], ya[1], ya[2], ya[3]};
+      *reinterpret_cast<uint4*>(k_ring + row + d0 + kHalf) = uint4{yb[0], yb[1], yb[2], yb[3]};
+    } else if (tid < kHalf / 8 + kD / 8) {
+      const int d0 = 8 * (tid - kHalf / 8);
+      *reinterpret_cast<uint4*>(v_ring + row + d0) = *reinterpret_cast<const uint4*>(v_new + src + d0);
+    }
+  }
+  // The new row is read below by other waves of this workgroup only: the barrier's
+  // workgroup-scope release and acquire make it visible (the waves share one CU), with no
+  // device-scope fence, which would write back and invalidate L2.
+  __syncthreads();
+
+  // Q^T operand as in the split kernel (loaded first, above), rotated with the shared table.
+  if (qlane) {
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      const bf16x8 xa = qf[dc], xb = qf[dc + 4];
+      f32x4 ya0, ya1, yb0, yb1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x2 c = cs[32 * dc + 8 * g + e];
+        float ya, yb;
+        rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
+        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
+      }
+      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
+      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
+      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      qf[dc + 4] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    }
+  }
+
+  const int kv_len = p >= 0 ? min(p + 1, kSlots) : 0;
+  const int k_begin = kPerWave * w;
+  const int k_end = min(kv_len, k_begin + kPerWave);
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[kGroup][8];
+#pragma unroll
+  for (int hl = 0; hl < kGroup; ++hl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
+  attend_keys(qf, k_ring + ring_off, v_ring + ring_off, k_begin, k_end, sl2, p_lds[w], lane,
+              m_run, l_run, o);
+#pragma unroll
+  for (int hl = 0; hl < kGroup; ++hl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] += __shfl_xor(o[hl][e], 32);
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (half == 0) {
+#pragma unroll
+    for (int hl = 0; hl < kGroup; ++hl) {
+      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg]) = f32x4{o[hl][0], o[hl][1], o[hl][2], o[hl][3]};
+      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg + 4]) = f32x4{o[hl][4], o[hl][5], o[hl][6], o[hl][7]};
+    }
+  }
+  if (lane < kGroup) {
+    part_ml[w][lane][0] = m_run;
+    part_ml[w][lane][1] = l_run;
+  }
+  __syncthreads();
+
+  // Merge: thread (head hl, dims 4j .. 4j + 3).
+  const int hl = tid >> 6, d = 4 * (tid & 63);
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kRingWaves; ++v) M = fmaxf(M, part_ml[v][hl][0]);
+  const float M_use = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  f32x4 acc = f32x4{};
+#pragma unroll
+  for (int v = 0; v < kRingWaves; ++v) {
+    const float wgt = fast_exp2(part_ml[v][hl][0] - M_use);
+    L += part_ml[v][hl][1] * wgt;
+    acc += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d]) * wgt;
+  }
+  const long long row = (long long)b * kHq + kvh * kGroup + hl;
+  const float gl = bf16_to_f32(gate[row]);
+  const float sg = 1.f / (1.f + expf(-gl));
+  const float f = L > 0.f ? sg / L : 0.f;
+  *reinterpret_cast<uint2*>(out + row * kD + d) =
+      uint2{pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f)};
+  if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int B, int max_keys) {
@@ -582,6 +768,15 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * kHq), kD / kCombDims), dim3(256), 0,
                      stream, ws_o, ws_ml, plan.nchunks, gate, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
+                            bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,
+                            const bf16_t* gate, bf16_t* out, float* lse, const RopeTable& tab,
+                            float scale_log2e, hipStream_t stream) {
+  hipLaunchKernelGGL(ring_step_kernel, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves), 0, stream, q, k_new,
+                     v_new, k_ring, v_ring, pos, gate, out, lse, tab, scale_log2e);
   return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@
 
 #include "hattn_device.h"
 
+struct hattn_layer_cfg;  // the C ABI's layer configuration
+
 namespace hattn {
 
 // Record e as the calling thread's last HIP error and return HATTN_ERR_HIP (api.hip).
@@ -42,6 +44,11 @@ hipError_t launch_prefill_ring(const bf16_t* q, const bf16_t* k_new, const bf16_
                                bool rope_q, const RopeTable& tab, float scale_log2e,
                                hipStream_t stream);
 
+// RoPE inverse frequencies and the softmax scale times log2(e) of a validated layer
+// configuration (the ABI layer builds these for every call).
+RopeTable rope_table(const ::hattn_layer_cfg* cfg);
+float scale_log2e(const ::hattn_layer_cfg* cfg);
+
 // Split-KV decode geometry, a pure function of (B, max keys per sequence).
 struct DecodePlan {
   int nchunks;  // key chunks per sequence
@@ -54,6 +61,15 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
                          const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
                          int window, bool rope_q, const RopeTable& tab, float scale_log2e,
                          const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+// One decode step of a sliding layer in one launch: rotate K by pos and append K / V at
+// ring slot pos mod 512 of k_ring / v_ring [B, 512, 4, 256], then attend (Q-RoPE fused),
+// gate and store out [B, 1, 16, 256] (and lse [B, 1, 16] unless null).  q, k_new, v_new
+// are the token's un-rotated projections [B, 1, *, 256].  No workspace.
+hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
+                            bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,
+                            const bf16_t* gate, bf16_t* out, float* lse, const RopeTable& tab,
+                            float scale_log2e, hipStream_t stream);
 
 // 8-bit KV decode: caches [B, cap, 4, 256] E4M3 codes, scales [B, 4, cap] fp32; same plan
 // and workspace as launch_decode.

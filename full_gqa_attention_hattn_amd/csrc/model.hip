@@ -88,14 +88,29 @@ hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, 
   if (workspace == nullptr || workspace_bytes < hattn_model_decode_workspace_bytes(n_layers, B, cap))
     return HATTN_ERR_WORKSPACE;
   if (!a16(workspace) || (reinterpret_cast<uintptr_t>(pos) & 3u)) return HATTN_ERR_ALIGN;
+  hattn_layer_cfg sliding;
+  hattn_cfg_preset(HATTN_SLIDING, &sliding);
+  const hattn::RopeTable sliding_tab = hattn::rope_table(&sliding);
+  const float sliding_scale = hattn::scale_log2e(&sliding);
   for (int32_t l = 0; l < n_layers; ++l) {
     const hattn_layer_io& L = layers[l];
     hattn_layer_cfg cfg;
     hattn_cfg_preset(kind_of(l), &cfg);
-    const int32_t c = cfg.kind == HATTN_FULL ? cap : kRing;
-    st = hattn_kv_append_rope(&cfg, L.k, L.v, L.k_cache, L.v_cache, c, pos, B, 1, nullptr, stream);
+    if (cfg.kind == HATTN_SLIDING) {
+      // Append, ring attention and merge in one launch (the 512-slot ring needs no split).
+      const hipError_t e = hattn::launch_ring_step(
+          static_cast<const hattn::bf16_t*>(L.q), static_cast<const hattn::bf16_t*>(L.k),
+          static_cast<const hattn::bf16_t*>(L.v), static_cast<hattn::bf16_t*>(L.k_cache),
+          static_cast<hattn::bf16_t*>(L.v_cache), pos, B,
+          static_cast<const hattn::bf16_t*>(L.gate), static_cast<hattn::bf16_t*>(L.out),
+          static_cast<float*>(L.lse), sliding_tab, sliding_scale,
+          reinterpret_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hattn::note_hip_error(e);
+      continue;
+    }
+    st = hattn_kv_append_rope(&cfg, L.k, L.v, L.k_cache, L.v_cache, cap, pos, B, 1, nullptr, stream);
     if (st != HATTN_OK) return st;
-    st = hattn_decode(&cfg, L.q, L.k_cache, L.v_cache, c, pos, B, L.gate, L.out, L.lse, workspace,
+    st = hattn_decode(&cfg, L.q, L.k_cache, L.v_cache, cap, pos, B, L.gate, L.out, L.lse, workspace,
                       workspace_bytes, HATTN_ROPE_Q_FUSED, stream);
     if (st != HATTN_OK) return st;
   }
