@@ -7,10 +7,10 @@
 // Both are Y = X W^T with X [T, K] and W [N, K] row-major (the linear-layer layout), so
 // both operands are rows with K contiguous.  A workgroup computes the 128 x 128 tile
 // Y^T[n][t] = sum_k W[n][k] X[t][k] on v_mfma_f32_32x32x16_bf16 (A = W rows, B = X rows),
-// four waves of 64 x 64.  64-wide K slices of both operands go global -> LDS directly
-// (global_load_lds_dwordx4), double-buffered, each 128-byte row with its 16-byte blocks
-// XOR-swizzled by (row >> 1) & 7 so that the 16 rows one 16-lane group reads hit 16
-// different bank groups.  Each MFMA of a 16-wide k-step is paired with one fragment read
+// four waves of 64 x 64.  64-wide K slices of both operands go global -> LDS directly (the
+// buffer form of the LDS copy, which keeps the fragment reads' LDS waits exact),
+// double-buffered, each 128-byte row with its 16-byte blocks XOR-swizzled by (row >> 1) & 7
+// so that the 16 rows one 16-lane group reads hit 16 different bank groups.  Each MFMA of a 16-wide k-step is paired with one fragment read
 // of the next k-step.  Tiles are ordered so that each XCD works on a band of token tiles
 // across all feature tiles (L2 reuse of both operands; +16% on the 4096-token QKV case).  The accumulator holds 4 consecutive output features of one
 // token per lane group, stored as 8-byte bf16 runs.  The fused projection's epilogue writes
@@ -25,33 +25,50 @@ namespace {
 
 constexpr int kTile = 128;            // output features and tokens per workgroup
 constexpr int kBK = 64;               // K per stage
+constexpr int kStages = 2;            // K slices resident in LDS (measured: 3-5 slower)
+constexpr int kRowB = kBK * 2;        // bytes of one row segment
+constexpr int kBlk = kRowB / 16;      // 16-byte blocks per row segment
 constexpr int kTileBytes = kTile * kBK * 2;
+constexpr int kLoadsPerSlice = kTileBytes / 1024 / 4;  // copy instructions per wave per slice
 constexpr int kQDim = kHq * kD, kKvDim = kHkv * kD, kQkvDim = kQDim + 2 * kKvDim;
 constexpr int kGateRows = kHq;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void g_void;
 
-__device__ __forceinline__ int pswz(int r) { return (r >> 1) & 7; }
+// Row r's 16-byte block b sits at b ^ pswz(r): the 16 rows one 16-lane group reads (at one
+// block) then fall on 16 different bank groups.
+__device__ __forceinline__ int pswz(int r) { return kBlk == 8 ? (r >> 1) & 7 : (r >> 2) & 3; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Rows row0 .. row0 + 127 (rows past `last` read row `last`), K k0 .. k0 + 63 of a
-// row-major [rows, K] matrix into LDS.  16 instructions of 1 KiB (8 rows each); wave w
-// issues 4w .. 4w + 3.  Lane l of instruction j lands at row 8j + l/8, physical block l%8,
-// so it fetches logical block (l%8) ^ pswz(row): 8 lanes read one 128-byte row segment.
+// Rows row0 .. row0 + 127 (rows past `last` read row `last`), K k0 .. k0 + kBK - 1 of a
+// row-major [rows, K] matrix into LDS with the buffer form of the global->LDS copy.  The
+// slice is kTileBytes / 1024 instructions of 1 KiB; wave w issues its kLoadsPerSlice.
+// Lane l of instruction j lands at row (1024 j + 16 l) / kRowB, physical block l % kBlk,
+// so it fetches the logical block (l % kBlk) ^ pswz(row).
 __device__ __forceinline__ void load_slice(char* dst, const bf16_t* base, long long ld, int row0,
                                            int last, int k0, int w, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(base + (long long)row0 * ld + k0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = 4 * w + i;
-    const int row = 8 * j + (lane >> 3);
-    const int lb = (lane & 7) ^ pswz(row);
-    const long long r = min(row0 + row, last);
-    __builtin_amdgcn_global_load_lds((g_void*)(base + r * ld + k0 + 8 * lb),
-                                     (lds_void*)(dst + j * 1024), 16, 0, 0);
+  for (int i = 0; i < kLoadsPerSlice; ++i) {
+    const int j = kLoadsPerSlice * w + i;
+    const int row = (1024 * j + 16 * lane) / kRowB;
+    const int lb = (lane % kBlk) ^ pswz(row);
+    const int r = min(row0 + row, last) - row0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * 1024), 16,
+                                             (int)((long long)r * ld * 2 + 16 * lb), 0, 0, 0);
   }
 }
 
@@ -63,7 +80,7 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
                                                    bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
                                                    bf16_t* __restrict__ y2,
                                                    bf16_t* __restrict__ y3, int nN, int nT) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * 2 * kTileBytes];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wn = wv & 1, wt = wv >> 1;
   // Tile order: with 8+ token tiles, XCD x (blockIdx % 8) owns a contiguous band of token
@@ -118,14 +135,28 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
     load_slice(st, wbase, K, wrow0, wlast, kt * kBK, wv, lane);
     load_slice(st + kTileBytes, x, K, t_tile, T - 1, kt * kBK, wv, lane);
   };
-  load_stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Stages 0 .. kStages - 2 in flight; stage kt + kStages - 1 is issued while kt computes.
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < nk) load_stage(i, i);
+  // Wait until slice `need` has landed: the slices issued after it may stay in flight.
+  // Slices 0 .. min(nk - 1, need + kStages - 2) have been issued when this runs.
+  static_assert(kStages >= 2 && kStages <= 5, "wait_slice covers up to 3 later slices");
+  auto wait_slice = [&](int need) {
+    const int after = min(nk - 1, need + kStages - 2) - need;  // issued later than `need`
+    constexpr int L = 2 * kLoadsPerSlice;
+    if (after >= kStages - 2) wait_vm<(kStages - 2) * L>();
+    else if (after == 2) wait_vm<2 * L>();
+    else if (after == 1) wait_vm<L>();
+    else wait_vm<0>();
+  };
+  wait_slice(0);
   __syncthreads();
 
   const int r32 = lane & 31, hk = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_stage((kt + 1) & 1, kt + 1);
-    const char* ws = smem + (kt & 1) * 2 * kTileBytes;
+    if (kt + kStages - 1 < nk) load_stage((kt + kStages - 1) % kStages, kt + kStages - 1);
+    const char* ws = smem + (kt % kStages) * 2 * kTileBytes;
     const char* xs = ws + kTileBytes;
     // Fragment f of k-step kk: f = 0, 1 are W rows (a), f = 2, 3 are X rows (b).  Each MFMA
     // of k-step kk is paired with one read of k-step kk + 1, so reads run a k-step ahead.
@@ -133,7 +164,7 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
       const int lb = 2 * kk + hk;
       const int row = f < 2 ? 64 * wn + 32 * f + r32 : 64 * wt + 32 * (f - 2) + r32;
       const char* base = f < 2 ? ws : xs;
-      return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((lb ^ pswz(row)) << 4));
+      return *reinterpret_cast<const bf16x8*>(base + row * kRowB + ((lb ^ pswz(row)) << 4));
     };
     bf16x8 cur[4], nxt[4];
 #pragma unroll
@@ -151,12 +182,12 @@ __global__ __launch_bounds__(256) void proj_kernel(const bf16_t* __restrict__ x,
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 4 * (kBK / 16) - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next stage has landed
+    if (kt + 1 < nk) wait_slice(kt + 1);
     __syncthreads();
   }
 
