@@ -105,3 +105,33 @@ def test_projections_chunk_4096(h):
     ry = O.o_proj(_cpu(a)[rows], _cpu(w_o))
     assert_bf16_close(_cpu(y)[rows], ry, "o_proj T=4096")
     _rel_l2(_cpu(y)[rows], ry, "o_proj T=4096")
+
+
+@pytest.mark.parametrize("T", [2048, 2100, 4000, 4096])
+def test_projections_every_output_written(h, T):
+    """Token counts where the 192 x 256 / 160 x 256 tiles (and the separate gate rows) may be
+    chosen, with ragged last tiles: outputs start as NaN, every element must be written, and
+    sampled rows at tile edges match the oracle."""
+    say(f"projections coverage T={T}")
+    w_qkv, w_g, w_o = _weights(191)
+    x = synth.normal_bf16((T, O.HIDDEN), 192, "cuda")
+    nan = float("nan")
+    q = torch.full((T, 16, 256), nan, dtype=torch.bfloat16, device="cuda")
+    k = torch.full((T, 4, 256), nan, dtype=torch.bfloat16, device="cuda")
+    v = torch.full((T, 4, 256), nan, dtype=torch.bfloat16, device="cuda")
+    g = torch.full((T, 16), nan, dtype=torch.bfloat16, device="cuda")
+    h.qkv_proj(x, w_qkv, w_g, q, k, v, g)
+    a = synth.normal_bf16((T, 16, 256), 193, "cuda")
+    y = torch.full((T, O.HIDDEN), nan, dtype=torch.bfloat16, device="cuda")
+    h.o_proj(a, w_o, y)
+    torch.cuda.synchronize()
+    for name, got in (("q", q), ("k", k), ("v", v), ("gate", g), ("o_proj", y)):
+        assert not bool(torch.isnan(got).any()), f"{name} T={T}: unwritten outputs"
+    last = (T - 1) // 256 * 256
+    rows = torch.tensor(sorted({0, 1, 127, 128, 255, 256, 257, T // 2, last - 1, last, T - 2, T - 1}))
+    rq, rk, rv, rg = O.qkv_proj(_cpu(x)[rows], _cpu(w_qkv), _cpu(w_g))
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv), ("gate", g, rg)):
+        assert_bf16_close(_cpu(got)[rows], ref, f"{name} T={T}")
+    ry = O.o_proj(_cpu(a)[rows], _cpu(w_o))
+    assert_bf16_close(_cpu(y)[rows], ry, f"o_proj T={T}")
+    _rel_l2(_cpu(y)[rows], ry, f"o_proj T={T}")
