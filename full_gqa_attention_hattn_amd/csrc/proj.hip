@@ -312,7 +312,7 @@ __global__ __launch_bounds__(S::kThreads) void proj_kernel(
 
 // Small T (decode steps, T <= 32), and the 16 gate rows next to the 192 x 256 tiles: the
 // work is split by output feature, token block and K instead.  A workgroup owns 16 features
-// of up to 32 tokens; wave w takes K quarter w and runs
+// of up to 32 tokens; wave w of its kKW takes the w-th K range and runs
 // v_mfma_f32_16x16x32_bf16 with A = 16 weight rows and B = up to 16 tokens per block, both
 // fragments loaded straight from global memory (16 bytes per lane, 4 k-steps in flight).
 // The four partial tiles are summed through LDS and wave 0 stores them.
@@ -323,12 +323,12 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int kFused, int kTB>
-__global__ __launch_bounds__(256) void proj_small_kernel(
+template <int kFused, int kTB, int kKW = 4, int kUnroll = 4>
+__global__ __launch_bounds__(64 * kKW) void proj_small_kernel(
     const bf16_t* __restrict__ x, int T, int K, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ w_gate, int N, bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
     bf16_t* __restrict__ y2, bf16_t* __restrict__ y3, int n_base) {
-  __shared__ f32x4 red[4][kTB][64];
+  __shared__ f32x4 red[kKW][kTB][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n0 = n_base + blockIdx.x * kSmallRows;
   const int t0 = blockIdx.y * 16 * kTB;  // this workgroup's tokens: t0 .. t0 + 16 kTB - 1
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void proj_small_kernel(
     else { dst = y2; dcol0 = n0 - kQDim - kKvDim; dld = kKvDim; }
   }
   const int r16 = lane & 15, kg = lane >> 4;   // fragment row / column and k-group
-  const int kq = K / 4;                        // this wave's K range
+  const int kq = K / kKW;                      // this wave's K range
   const bf16_t* wr = wbase + (long long)(wrow + r16) * K + wv * kq + 8 * kg;
   const bf16_t* xr[kTB];
 #pragma unroll
@@ -354,7 +354,6 @@ __global__ __launch_bounds__(256) void proj_small_kernel(
   f32x4 acc[kTB];
 #pragma unroll
   for (int tb = 0; tb < kTB; ++tb) acc[tb] = f32x4{};
-  constexpr int kUnroll = 4;
   for (int k = 0; k < kq; k += 32 * kUnroll) {
     bf16x8 a[kUnroll], b[kUnroll][kTB];
 #pragma unroll
@@ -375,7 +374,9 @@ __global__ __launch_bounds__(256) void proj_small_kernel(
   // acc element j: feature n0 + 4 kg + j, token 16 tb + r16.
 #pragma unroll
   for (int tb = 0; tb < kTB; ++tb) {
-    const f32x4 v = red[0][tb][lane] + red[1][tb][lane] + red[2][tb][lane] + red[3][tb][lane];
+    f32x4 v = red[0][tb][lane];
+#pragma unroll
+    for (int i = 1; i < kKW; ++i) v += red[i][tb][lane];
     const int t = 16 * tb + r16;
     if (t >= T) continue;
     const uint2 o{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -383,20 +384,31 @@ __global__ __launch_bounds__(256) void proj_small_kernel(
   }
 }
 
-// Features n_base .. n_base + rows - 1 (a multiple of 16) of all T tokens, in workgroups of
-// 16 features x 32 tokens.
+// Features n_base .. n_base + rows - 1 (a multiple of 16) of all T <= 32 tokens.
 template <int kFused>
 hipError_t launch_small(const bf16_t* x, int T, int K, const bf16_t* w, const bf16_t* w_gate,
                         int N, bf16_t* y0, bf16_t* y1, bf16_t* y2, bf16_t* y3, int n_base,
                         int rows, hipStream_t stream) {
-  if (T <= 16) {
-    hipLaunchKernelGGL((proj_small_kernel<kFused, 1>), dim3((unsigned)(rows / kSmallRows)),
-                       dim3(256), 0, stream, x, T, K, w, w_gate, N, y0, y1, y2, y3, n_base);
-  } else {
-    const dim3 grid((unsigned)(rows / kSmallRows), (unsigned)((T + 31) / 32));
+  const dim3 grid((unsigned)(rows / kSmallRows));
+  if (T <= 16)
+    hipLaunchKernelGGL((proj_small_kernel<kFused, 1>), grid, dim3(256), 0, stream, x, T, K, w,
+                       w_gate, N, y0, y1, y2, y3, n_base);
+  else
     hipLaunchKernelGGL((proj_small_kernel<kFused, 2>), grid, dim3(256), 0, stream, x, T, K, w,
                        w_gate, N, y0, y1, y2, y3, n_base);
-  }
+  return hipGetLastError();
+}
+
+// The 16 gate rows of all T tokens: a workgroup per 16 tokens, whose 8 waves split K = 2560
+// into ranges of 320 and issue all their loads at once (the kernel streams X once and is
+// bound by load latency).
+hipError_t launch_gate_rows(const bf16_t* x, int T, const bf16_t* w_gate, bf16_t* gate,
+                            hipStream_t stream) {
+  constexpr int kKW = 8, kUnroll = kProjHidden / kKW / 32;
+  static_assert(kUnroll * 32 * kKW == kProjHidden, "K splits into whole 32-wide steps");
+  hipLaunchKernelGGL((proj_small_kernel<1, 1, kKW, kUnroll>), dim3(1, (unsigned)((T + 15) / 16)),
+                     dim3(64 * kKW), 0, stream, x, T, kProjHidden, nullptr, w_gate,
+                     kQkvDim + kGateRows, nullptr, nullptr, nullptr, gate, kQkvDim);
   return hipGetLastError();
 }
 
@@ -450,8 +462,7 @@ hipError_t launch_qkv_proj(const bf16_t* x, int T, const bf16_t* w_qkv, const bf
   const int cus = cu_count();
   if (tile_cost<TileQ>(kQkvDim, T, cus, 3.8) < tile_cost<TileA>(N, T, cus, 4.1)) {
     // The 6144 q/k/v rows on 192 x 256 tiles, the 16 gate rows on the small kernel.
-    const hipError_t e = launch_small<1>(x, T, kProjHidden, w_qkv, w_gate, N, q, k, v, gate,
-                                         kQkvDim, kGateRows, stream);
+    const hipError_t e = launch_gate_rows(x, T, w_gate, gate, stream);
     if (e != hipSuccess) return e;
     return launch_tiles<1, TileQ>(x, T, kProjHidden, w_qkv, w_gate, kQkvDim, q, k, v, gate,
                                   stream);
