@@ -314,8 +314,8 @@ __global__ __launch_bounds__(S::kThreads) void proj_kernel(
 // work is split by output feature, token block and K instead.  A workgroup owns 16 features
 // of up to 32 tokens; wave w of its kKW takes the w-th K range and runs
 // v_mfma_f32_16x16x32_bf16 with A = 16 weight rows and B = up to 16 tokens per block, both
-// fragments loaded straight from global memory (16 bytes per lane, 4 k-steps in flight).
-// The four partial tiles are summed through LDS and wave 0 stores them.
+// fragments loaded straight from global memory (16 bytes per lane, kUnroll k-steps in
+// flight).  The kKW partial tiles are summed through LDS and wave 0 stores them.
 constexpr int kSmallRows = 16;
 constexpr int kSmallMaxT = 32;
 
