@@ -330,8 +330,9 @@ __global__ __launch_bounds__(64 * kKW) void proj_small_kernel(
     bf16_t* __restrict__ y2, bf16_t* __restrict__ y3, int n_base) {
   __shared__ f32x4 red[kKW][kTB][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n0 = n_base + blockIdx.x * kSmallRows;
-  const int t0 = blockIdx.y * 16 * kTB;  // this workgroup's tokens: t0 .. t0 + 16 kTB - 1
+  // Grid: x = token blocks (up to 2^31 - 1 of them), y = 16-feature blocks.
+  const int n0 = n_base + blockIdx.y * kSmallRows;
+  const int t0 = blockIdx.x * 16 * kTB;  // this workgroup's tokens: t0 .. t0 + 16 kTB - 1
   x += (long long)t0 * K;
   T -= t0;
   const bf16_t* wbase = w;
@@ -389,7 +390,7 @@ template <int kFused>
 hipError_t launch_small(const bf16_t* x, int T, int K, const bf16_t* w, const bf16_t* w_gate,
                         int N, bf16_t* y0, bf16_t* y1, bf16_t* y2, bf16_t* y3, int n_base,
                         int rows, hipStream_t stream) {
-  const dim3 grid((unsigned)(rows / kSmallRows));
+  const dim3 grid(1, (unsigned)(rows / kSmallRows));
   if (T <= 16)
     hipLaunchKernelGGL((proj_small_kernel<kFused, 1>), grid, dim3(256), 0, stream, x, T, K, w,
                        w_gate, N, y0, y1, y2, y3, n_base);
@@ -406,7 +407,7 @@ hipError_t launch_gate_rows(const bf16_t* x, int T, const bf16_t* w_gate, bf16_t
                             hipStream_t stream) {
   constexpr int kKW = 8, kUnroll = kProjHidden / kKW / 32;
   static_assert(kUnroll * 32 * kKW == kProjHidden, "K splits into whole 32-wide steps");
-  hipLaunchKernelGGL((proj_small_kernel<1, 1, kKW, kUnroll>), dim3(1, (unsigned)((T + 15) / 16)),
+  hipLaunchKernelGGL((proj_small_kernel<1, 1, kKW, kUnroll>), dim3((unsigned)((T + 15) / 16)),
                      dim3(64 * kKW), 0, stream, x, T, kProjHidden, nullptr, w_gate,
                      kQkvDim + kGateRows, nullptr, nullptr, nullptr, gate, kQkvDim);
   return hipGetLastError();

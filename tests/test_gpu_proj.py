@@ -135,3 +135,24 @@ def test_projections_every_output_written(h, T):
     ry = O.o_proj(_cpu(a)[rows], _cpu(w_o))
     assert_bf16_close(_cpu(y)[rows], ry, f"o_proj T={T}")
     _rel_l2(_cpu(y)[rows], ry, f"o_proj T={T}")
+
+
+def test_projections_past_a_million_tokens(h):
+    """T = 2^20 + 40 tokens: more token blocks than a grid's y extent holds, so the launch
+    geometry of every kernel the shape choice can pick is exercised at this size (about 32 GB
+    of activations); sampled rows at the start and at the ragged end match the oracle."""
+    T = (1 << 20) + 40
+    say(f"projections T={T}")
+    w_qkv, w_g, w_o = _weights(196)
+    x = synth.normal_bf16((T, O.HIDDEN), 197, "cuda")
+    q, k, v, g = _run_qkv(h, x, w_qkv, w_g)
+    a = synth.normal_bf16((T, 16, 256), 198, "cuda")
+    y = torch.empty(T, O.HIDDEN, dtype=torch.bfloat16, device="cuda")
+    h.o_proj(a, w_o, y)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 255, 256, T // 2, T - 41, T - 40, T - 2, T - 1])
+    rq, rk, rv, rg = O.qkv_proj(_cpu(x[rows]), _cpu(w_qkv), _cpu(w_g))
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv), ("gate", g, rg)):
+        assert_bf16_close(_cpu(got[rows.cuda()]), ref, f"{name} T={T}")
+    ry = O.o_proj(_cpu(a[rows.cuda()]), _cpu(w_o))
+    assert_bf16_close(_cpu(y[rows.cuda()]), ry, f"o_proj T={T}")
