@@ -40,7 +40,9 @@ hattn_status check_layers(const hattn_layer_io* layers, int32_t n_layers) {
 }
 
 hattn_status check_common(const hattn_layer_io* layers, int32_t n_layers, int32_t B, int32_t cap) {
-  if (n_layers < 1 || n_layers > kMaxLayers || B < 0 || cap < kRing) return HATTN_ERR_SHAPE;
+  // Batch is a grid dimension (y) of the per-layer launches, whose extent stops at 65535.
+  if (n_layers < 1 || n_layers > kMaxLayers || B < 0 || B > 65535 || cap < kRing)
+    return HATTN_ERR_SHAPE;
   if (layers == nullptr) return HATTN_ERR_NULL;
   return HATTN_OK;
 }

@@ -175,6 +175,7 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
  * Same arithmetic as hattn_prefill.  The key range is split into chunks whose partial
  * (max, sum, output) triples are merged by log-sum-exp in a second kernel.
  * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes.
+ * B <= 65535 (one grid row per sequence), else HATTN_ERR_SHAPE.
  * [T2] "The real bottleneck of a million-token context" (the ring keeps the last 512
  * tokens); [T1] "GQA, fused projection and output gating". */
 hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
@@ -257,7 +258,8 @@ size_t hattn_model_decode_workspace_bytes(int32_t n_layers, int32_t B, int32_t c
  * attended (hattn_decode with HATTN_ROPE_Q_FUSED).  layers: host array of n_layers.
  * Nothing is allocated and no input is modified, so a captured step replays exactly.
  * All pointers are checked before anything is enqueued; a later non-OK status can only
- * be HATTN_ERR_HIP.  Errors: those of the per-layer calls, HATTN_ERR_WORKSPACE. */
+ * be HATTN_ERR_HIP.  Errors: those of the per-layer calls, HATTN_ERR_WORKSPACE, and
+ * HATTN_ERR_SHAPE unless 1 <= n_layers <= 4096, 0 <= B <= 65535, cap >= 512. */
 hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, int32_t cap,
                                 const int32_t* pos, int32_t B, void* workspace,
                                 size_t workspace_bytes, void* stream);
@@ -269,7 +271,8 @@ size_t hattn_model_prefill_workspace_bytes(int32_t n_layers, int32_t B, int32_t 
  *   full:    hattn_kv_append_rope into the cache, then hattn_prefill over it;
  *   sliding: the chunk's keys are rotated into the workspace, attended together with the
  *            ring (hattn_prefill_ring), then appended to the ring.
- * Chunks must arrive in position order, each after the previous one's call. */
+ * Chunks must arrive in position order, each after the previous one's call.
+ * HATTN_ERR_SHAPE unless 1 <= n_layers <= 4096, 0 <= B <= 65535, cap >= 512, Sq >= 0. */
 hattn_status hattn_model_prefill(const hattn_layer_io* layers, int32_t n_layers, int32_t cap,
                                  const int32_t* pos0, int32_t B, int32_t Sq, void* workspace,
                                  size_t workspace_bytes, void* stream);

@@ -224,6 +224,7 @@ def test_model_validation(h):
                                              o.get("wsb", need), None)
     assert dec(n=0) == h.HATTN_ERR_SHAPE
     assert dec(cap=511) == h.HATTN_ERR_SHAPE
+    assert dec(B=65536) == h.HATTN_ERR_SHAPE          # a grid's y extent; no layer is enqueued
     assert dec(io=None) == h.HATTN_ERR_NULL
     assert dec(pos=None) == h.HATTN_ERR_NULL
     assert dec(ws=None) == h.HATTN_ERR_WORKSPACE
@@ -243,6 +244,7 @@ def test_model_validation(h):
     pre = lambda **o: lib.hattn_model_prefill(io, 4, 1024, o.get("pos", A), 2, o.get("S", 40),
                                               o.get("ws", A), o.get("wsb", pneed), None)
     assert pre(S=-1) == h.HATTN_ERR_SHAPE
+    assert lib.hattn_model_prefill(io, 4, 1024, A, 65536, 40, A, pneed, None) == h.HATTN_ERR_SHAPE
     assert pre(S=0) == h.HATTN_OK
     assert pre(pos=None) == h.HATTN_ERR_NULL
     assert pre(wsb=pneed - 16) == h.HATTN_ERR_WORKSPACE
