@@ -47,19 +47,35 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) { return __builtin_bit_ca
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// sin and cos of an fp32 angle, with an absolute error below 1e-7 for 0 <= x < 2^21 (checked
-// against fp64 sin and cos over every RoPE angle p * omega_i with p < 2^20 + 4096: 7.4e-8).
-// Range reduction: Cody and Waite's additive reduction by pi/2, in fp32 with a three-part
-// constant: C1 = fp32(pi/2), C2 = fp32(pi/2 - C1), C3 = -2^-49 the next piece.  Each product
-// k * Ci is exact inside its fma, and x - k * C1 is exact (a multiple of 2^-23 below 1 in
-// magnitude).  k = rint(x * 2/pi) rounded in fp32 can miss the nearest quadrant by a little,
-// so |r| <= 0.88; there the Taylor-Maclaurin series of sin to r^9 and of cos to r^10 are
-// truncated below 6e-9.
+// sin and cos of an fp32 angle, with an absolute error below 1e-7 (checked against fp64 sin
+// and cos over every RoPE angle p * omega_i with p < 2^20 + 4096: 7.4e-8).
+// Range reduction below 2^21: Cody and Waite's additive reduction by pi/2, in fp32 with a
+// three-part constant: C1 = fp32(pi/2), C2 = fp32(pi/2 - C1), C3 = -2^-49 the next piece.
+// Each product k * Ci is exact inside its fma, and x - k * C1 is exact (a multiple of 2^-23
+// below 1 in magnitude).  k = rint(x * 2/pi) rounded in fp32 can miss the nearest quadrant
+// by a little, so |r| <= 0.88.  From 2^21 on (positions past two million tokens) the fp32
+// quotient can miss the quadrant by many periods, so the reduction runs in fp64 instead:
+// k = rint(x * 2/pi) is exact there (x < 2^32), x - k * P1 with P1 = fp64(pi/2) is exact
+// inside its fma and rounded once, and P2 = pi/2 - P1 adds the remainder, which leaves r
+// within about 1e-16 of the true reduced angle.  On |r| <= 0.88 the Taylor-Maclaurin series
+// of sin to r^9 and of cos to r^10 are truncated below 6e-9.
 __device__ __forceinline__ void sincos_angle(float x, float* s_out, float* c_out) {
-  const float k = __builtin_rintf(__fmul_rn(x, 0.636619772f));  // 2/pi
-  float r = __builtin_fmaf(-k, 1.57079637f, x);                   // C1
-  r = __builtin_fmaf(-k, -4.37113883e-08f, r);                    // C2
-  r = __builtin_fmaf(-k, -1.77635684e-15f, r);                    // C3
+  float r;
+  int q;
+  if (__builtin_expect(x < 2097152.f, 1)) {
+    const float k = __builtin_rintf(__fmul_rn(x, 0.636619772f));  // 2/pi
+    r = __builtin_fmaf(-k, 1.57079637f, x);                         // C1
+    r = __builtin_fmaf(-k, -4.37113883e-08f, r);                    // C2
+    r = __builtin_fmaf(-k, -1.77635684e-15f, r);                    // C3
+    q = (int)k & 3;
+  } else {
+    const double xd = (double)x;
+    const double kd = __builtin_rint(xd * 0.63661977236758134308);   // 2/pi
+    double rd = __builtin_fma(-kd, 1.5707963267948966192, xd);      // P1
+    rd = __builtin_fma(-kd, 6.1232339957367660359e-17, rd);         // P2
+    r = (float)rd;
+    q = (int)((long long)kd & 3);
+  }
   const float r2 = r * r;
   // sin r = r (1 - r^2/3! + r^4/5! - r^6/7! + r^8/9!)
   float sp = 2.75573192e-06f;                        // 1/9!
@@ -74,7 +90,6 @@ __device__ __forceinline__ void sincos_angle(float x, float* s_out, float* c_out
   cp = __builtin_fmaf(cp, r2, 4.16666667e-02f);      // 1/4!
   cp = __builtin_fmaf(cp, r2, -0.5f);
   const float cs = __builtin_fmaf(cp, r2, 1.0f);
-  const int q = (int)k & 3;
   float s, c;
   switch (q) {
     case 0: s = sn; c = cs; break;

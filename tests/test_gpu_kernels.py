@@ -55,6 +55,31 @@ def test_rope_matches_oracle_up_to_1m_positions(h, kind):
             assert torch.equal(g[..., r:], _cpu(src)[..., r:])
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_rope_at_far_positions(h, kind):
+    """Positions far past the model's context, up to the largest the interface accepts
+    (2^31 - 1): angles beyond 2^21 take the fp64 range reduction, and a wrong quadrant or
+    reduction there would swap or negate sin and cos."""
+    say(f"rope far {kind}")
+    B, S = 3, 64
+    inp = synth.layer_inputs(12, B, S, "cuda")
+    pos0 = [(1 << 21) - 32, (1 << 30) + 3, (1 << 31) - S]   # last token of b=2: 2^31 - 1
+    cfg = h.preset(kind)
+    q, k = inp["q"].clone(), inp["k"].clone()
+    h.rope_qk(cfg, q, k, synth.positions(pos0, B, "cuda"))
+    torch.cuda.synchronize()
+    r = O.KINDS[kind].rot_dim
+    for b in range(B):
+        qr, kr = O.rope_qk(_cpu(inp["q"][b]), _cpu(inp["k"][b]), pos0[b], kind)
+        for name, g, ref in (("q", q[b], qr), ("k", k[b], kr)):
+            g = _cpu(g)
+            err = (g[..., :r].double() - ref[..., :r].double()).abs()
+            assert float((err - (2 ** -8) * ref[..., :r].double().abs() - 1e-5).max()) <= 0, \
+                f"{name} b={b} pos0={pos0[b]}"
+            exact = (g[..., :r] == ref[..., :r].to(torch.bfloat16)).double().mean()
+            assert float(exact) > 0.98, f"{name} b={b}: only {float(exact):.3f} round-to-nearest"
+
+
 # ---------------------------------------------------------------------- KV append --
 def test_append_full_cache_slots_and_bits(h):
     say("append full")
