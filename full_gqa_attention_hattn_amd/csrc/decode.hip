@@ -187,8 +187,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int n16 = lane & 15, g = lane >> 4;    // MFMA view: column (head) and k-group
   const int half = lane >> 5, dg = lane & 31;  // PV view: key parity and 8-dim group
   const int p = pos[b];
-  int kv_len = kSliding ? min(p + 1, window) : p + 1;
-  kv_len = max(0, min(kv_len, cap));
+  // Keys 0 .. p (the last window of them on sliding layers), within the cache; formed
+  // without p + 1, which overflows at the largest position.
+  const int kv_len = p < 0 ? 0 : min(min(p, (kSliding ? window : cap) - 1) + 1, cap);
   const int k_begin = c * chunk;
   const int k_end = min(kv_len, k_begin + chunk);
 
@@ -283,8 +284,9 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
   const int n16 = lane & 15, g = lane >> 4;    // MFMA view: column (head) and k-group
   const int kq = lane >> 4, dg = lane & 15;    // PV view: key phase and 16-dim group
   const int p = pos[b];
-  int kv_len = kSliding ? min(p + 1, window) : p + 1;
-  kv_len = max(0, min(kv_len, cap));
+  // Keys 0 .. p (the last window of them on sliding layers), within the cache; formed
+  // without p + 1, which overflows at the largest position.
+  const int kv_len = p < 0 ? 0 : min(min(p, (kSliding ? window : cap) - 1) + 1, cap);
   const int k_begin = c * chunk;
   const int k_end = min(kv_len, k_begin + chunk);
 
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
     }
   }
 
-  const int kv_len = p >= 0 ? min(p + 1, kSlots) : 0;
+  const int kv_len = p >= 0 ? min(p, kSlots - 1) + 1 : 0;  // no p + 1: p may be 2^31 - 1
   const int k_begin = kPerWave * w;
   const int k_end = min(kv_len, k_begin + kPerWave);
   float m_run = -INFINITY, l_run = 0.f;

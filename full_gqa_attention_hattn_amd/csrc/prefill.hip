@@ -347,8 +347,8 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
     const int key0 = t * kBN;
-    const bool whole = (key0 + kBN - 1 <= Pw0) && (key0 + kBN <= capk) &&
-                       (!kSliding || Pwl - key0 <= window - 1);
+    const bool whole = (key0 <= Pw0 - (kBN - 1)) && (key0 <= capk - kBN) &&  // no key0 + kBN:
+                       (!kSliding || Pwl - key0 <= window - 1);    // it overflows near 2^31
     if (!whole) {
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {

@@ -86,7 +86,8 @@ typedef struct hattn_layer_cfg {
 hattn_status hattn_cfg_preset(int32_t kind, hattn_layer_cfg* out);
 
 /* RoPE, in place, on q [B,S,16,256] and/or k [B,S,4,256] (either may be NULL, not both).
- * Token s of sequence b sits at position pos0[b] + s (pos0: int32 [B], device).
+ * Token s of sequence b sits at position pos0[b] + s (pos0: int32 [B], device); positions
+ * are int32, so pos0[b] + S - 1 <= 2^31 - 1 (checked nowhere: pos0 lives on the device).
  * Pair (i, i + r/2), i < r/2 with r = rot_dim, turns by angle
  *   a = float32( float32(pos) * float32(theta ** (-2 i / r)) )
  * (rotate-half pairing); dims r..255 are neither read nor written.  fp32 arithmetic,
@@ -97,7 +98,8 @@ hattn_status hattn_rope_qk(const hattn_layer_cfg* cfg, void* q, void* k, const i
                            int32_t B, int32_t S, void* stream);
 
 /* Copy n rotated tokens per sequence, k_new / v_new [B,n,4,256], into the caches
- * k_cache / v_cache [B,cap,4,256].  Token t of sequence b has position p = pos0[b] + t.
+ * k_cache / v_cache [B,cap,4,256].  Token t of sequence b has position p = pos0[b] + t,
+ * an int32: pos0[b] + n - 1 <= 2^31 - 1 (a larger value wraps negative and is skipped).
  *   full:    slot = p; tokens with p < 0 or p >= cap are skipped (slot reported -1).
  *   sliding: cap must equal cfg->window (the ring); slot = p mod window; when n > window
  *            only the last `window` tokens are written (a later token would overwrite

@@ -253,7 +253,9 @@ def test_decode_full_cache(h, fused):
 @pytest.mark.parametrize("fused", [True, False])
 def test_decode_ring(h, fused):
     say(f"decode ring fused={fused}")
-    _decode_case(h, "sliding", [0, 5, 510, 511, 512, 131072, (1 << 20)], 512, 81, fused)
+    # up to the largest int32 position, where p + 1 would overflow
+    _decode_case(h, "sliding", [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9,
+                                (1 << 31) - 1], 512, 81, fused)
 
 
 def test_decode_equals_prefill_row(h):

@@ -41,9 +41,10 @@ def _ring_state(seed, B, pos0):
 @pytest.mark.parametrize("fused", [True, False])
 def test_prefill_ring_matches_oracle(h, fused):
     """Ragged chunk (300 rows) at chunk starts inside the first window, exactly at a
-    wrap, past a wrap, unaligned to the 32-key tile, and at 128K."""
+    wrap, past a wrap, unaligned to the 32-key tile, at 128K, and far past the model's
+    context up to the last chunk the interface accepts (pos0 + Sq = 2^31 - 1)."""
     say(f"prefill_ring fused={fused}")
-    pos0 = [0, 37, 511, 512, 1000, 131072 - 45]
+    pos0 = [0, 37, 511, 512, 1000, 131072 - 45, (1 << 30) + 7, (1 << 31) - 1 - 300]
     B, Sq = len(pos0), 300
     cfg = h.preset("sliding")
     inp = synth.layer_inputs(101, B, Sq, "cuda")
