@@ -104,7 +104,7 @@ template <int kFused, class S>
 __global__ __launch_bounds__(S::kThreads) void proj_kernel(
     const bf16_t* __restrict__ x, int T, int K, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ w_gate, int N, bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
-    bf16_t* __restrict__ y2, bf16_t* __restrict__ y3, int nN, int nT) {
+    bf16_t* __restrict__ y2, bf16_t* __restrict__ y3, int nN, int nT, int gN) {
   constexpr int kAN = S::kAN, kAT = S::kAT, kGN = S::kGN, kWaves = S::kWaves;
   constexpr int kTN = S::kTN, kTT = S::kTT;
   constexpr int kF = kAN + kAT, kM = kAN * kAT;  // fragments and MFMAs per k-step
@@ -113,13 +113,21 @@ __global__ __launch_bounds__(S::kThreads) void proj_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStageBytes];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wn = wv % kGN, wt = wv / kGN;
-  // Tile order: with 8+ token tiles, XCD x (blockIdx % 8) owns a contiguous band of token
-  // tiles and walks all feature tiles across it, so the workgroups resident on one XCD
-  // share their X and W slices in its L2.
+  // Tile order.  Workgroup i runs on XCD i % 8.  With gN > 0 the 8 XCDs split the tiles
+  // into gN feature bands x 8 / gN token bands, and XCD x walks its band with the feature
+  // tile varying fastest, so each XCD's L2 fetches only its bands' slices of W and X (the
+  // launcher picks gN for the least fetched bytes).  Otherwise, with 8+ token tiles, XCD x
+  // owns a contiguous band of token tiles across all feature tiles.
   int nb, tb;
   {
     const int id = (int)blockIdx.x;
-    if (nT >= 8) {
+    if (gN > 0) {
+      const int xcd = id & 7, local = id >> 3;
+      const int bn = nN / gN, bt = nT / (8 / gN);
+      if (local >= bn * bt) return;
+      nb = (xcd % gN) * bn + local % bn;
+      tb = (xcd / gN) * bt + local / bn;
+    } else if (nT >= 8) {
       const int xcd = id & 7, local = id >> 3;
       const int per = (nT + 7) >> 3;
       const int t_lo = xcd * per;
@@ -413,8 +421,24 @@ hipError_t launch_gate_rows(const bf16_t* x, int T, const bf16_t* w_gate, bf16_t
   return hipGetLastError();
 }
 
-// Workgroups for nN x nT tiles: with the XCD banding, 8 bands of ceil(nT / 8) token tiles.
-long long grid_size(int nN, int nT) {
+// The XCD split for nN x nT tiles of tn x tt: the gN in {1, 2, 4, 8} dividing nN (with
+// 8 / gN dividing nT) that fetches the fewest bytes, W / gN + X / (8 / gN) per XCD; 0 when
+// none divides (then the token banding below is used).
+int xcd_split(int nN, int nT, int tn, int tt, int K) {
+  int best = 0;
+  double best_bytes = 0.0;
+  for (int g = 1; g <= 8; g *= 2) {
+    if (nN % g != 0 || nT % (8 / g) != 0) continue;
+    const double bytes = (double)nN * tn * K / g + (double)nT * tt * K / (8 / g);
+    if (best == 0 || bytes < best_bytes) { best = g; best_bytes = bytes; }
+  }
+  return best;
+}
+
+// Workgroups for nN x nT tiles: every tile once with an XCD split, else 8 bands of
+// ceil(nT / 8) token tiles (8+ token tiles) or one per tile.
+long long grid_size(int nN, int nT, int gN) {
+  if (gN > 0) return (long long)nN * nT;
   return nT >= 8 ? 8LL * nN * ((nT + 7) / 8) : (long long)nN * nT;
 }
 
@@ -423,8 +447,10 @@ hipError_t launch_tiles(const bf16_t* x, int T, int K, const bf16_t* w, const bf
                         int N, bf16_t* y0, bf16_t* y1, bf16_t* y2, bf16_t* y3,
                         hipStream_t stream) {
   const int nN = (N + S::kTN - 1) / S::kTN, nT = (T + S::kTT - 1) / S::kTT;
-  hipLaunchKernelGGL((proj_kernel<kFused, S>), dim3((unsigned)grid_size(nN, nT)),
-                     dim3(S::kThreads), 0, stream, x, T, K, w, w_gate, N, y0, y1, y2, y3, nN, nT);
+  const int gN = xcd_split(nN, nT, S::kTN, S::kTT, K);
+  hipLaunchKernelGGL((proj_kernel<kFused, S>), dim3((unsigned)grid_size(nN, nT, gN)),
+                     dim3(S::kThreads), 0, stream, x, T, K, w, w_gate, N, y0, y1, y2, y3, nN, nT,
+                     gN);
   return hipGetLastError();
 }
 
