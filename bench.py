@@ -739,7 +739,8 @@ def main():
         rec["o_proj_TFLOPs"] = to
         rec["roofline"] = {"bound": "mfma", "kernel": "proj_kernel (fused QKV + gate)",
                            "achieved": tq, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": tq / PEAK_BF16_TFLOPS, "traffic": None}
+                           "frac": tq / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic("proj.hip", "proj_qkv_t4096")}
     elif isinstance(wl, ModelWorkload):
         model_fields(rec, wl, ms, stage_ms)
     elif wl.prefill_flop:
