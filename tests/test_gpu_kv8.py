@@ -100,7 +100,9 @@ def _oracle_cache8(kc, vc):
 def test_decode_fp8_matches_oracle(h, kind, fused):
     say(f"decode_fp8 {kind} fused={fused}")
     cfg = h.preset(kind)
-    positions = [0, 31, 511, 512, 2999] if kind == "full" else [0, 5, 511, 512, 1 << 20]
+    # sliding: up to the largest int32 position (its key count must not overflow)
+    positions = ([0, 31, 511, 512, 2999] if kind == "full"
+                 else [0, 5, 511, 512, 1 << 20, (1 << 30) + 9, (1 << 31) - 1])
     B = len(positions)
     cap = 3000 if kind == "full" else 512
     new = synth.layer_inputs(173, B, 1, "cuda")
