@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 import synth
-from parity import check_outputs, say
+from parity import assert_bf16_close, check_outputs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +165,36 @@ def test_model_decode_graph_replay(h):
             vc[slot] = _cpu(L["v"][b, 0]).float()
             y, lse = O.decode(_cpu(L["q"][b, 0]), kc, vc, _cpu(L["gate"][b, 0]), p[b], kind)
             check_outputs(ref[l][0][b, 0], ref[l][1][b, 0], y, lse, f"graph layer {l} b={b}")
+
+
+def test_model_decode_sliding_at_far_positions(h):
+    """Three sliding layers (the fused ring step) at positions far past the model's context,
+    up to the largest int32 position: the rotated key lands in slot p mod 512 and the
+    token attends the whole ring, as the oracle's decode over the same ring."""
+    say("model decode far positions")
+    n_layers, B = 3, 2
+    positions = [(1 << 30) + 5, (1 << 31) - 1]
+    layers = _model_layers(h, n_layers, B, 1, 512, 171)
+    before = []
+    for l, L in enumerate(layers):
+        ring = synth.cache_inputs(172 + l, B, 512, 512, "cuda")
+        L["k_cache"].copy_(ring["cache_k"])
+        L["v_cache"].copy_(ring["cache_v"])
+        before.append((_cpu(L["k_cache"]).clone(), _cpu(L["v_cache"]).clone()))
+    ws = torch.empty(h.model_decode_workspace_bytes(n_layers, B, 512), dtype=torch.uint8,
+                     device="cuda")
+    h.model_decode(layers, 512, synth.positions(positions, B, "cuda"), ws)
+    torch.cuda.synchronize()
+    for l, L in enumerate(layers):
+        for b, p in enumerate(positions):
+            _, kr = O.rope_qk(None, _cpu(L["k"][b]), p, "sliding")
+            K, V = before[l][0][b].clone(), before[l][1][b].clone()
+            K[p % 512] = kr[0].to(torch.bfloat16)
+            V[p % 512] = _cpu(L["v"][b, 0])
+            got_k = _cpu(L["k_cache"][b])
+            assert torch.equal(got_k[torch.arange(512) != p % 512], K[torch.arange(512) != p % 512])
+            assert_bf16_close(got_k[p % 512], kr[0], f"ring key layer {l} p={p}")
+            assert torch.equal(_cpu(L["v_cache"][b]), V)
+            K[p % 512] = got_k[p % 512]          # attend over the ring the kernel wrote
+            y, lse = O.decode(_cpu(L["q"][b, 0]), K, V, _cpu(L["gate"][b, 0]), p, "sliding")
+            check_outputs(L["out"][b, 0], L["lse"][b, 0], y, lse, f"model far layer {l} p={p}")
