@@ -704,6 +704,215 @@ __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
   if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
+constexpr int kRingSlots = 512;                     // a sliding layer's ring
+constexpr int kRingSplits = 8;                      // workgroups per (KV head, sequence)
+constexpr int kSplitWaves = 2;                      // waves per split workgroup
+constexpr int kRingPerSplit = kRingSlots / kRingSplits;
+constexpr int kRingSplitMaxB = 2;                   // larger batches use the fused kernel
+static_assert(kRingPerSplit == kSplitWaves * kStep, "one 32-key step per wave");
+
+// The same step for small batches, where one workgroup per (KV head, sequence) leaves most
+// CUs idle: append, attention over the ring and the merge in one launch, with the ring's
+// 512 slots split over kRingSplits workgroups per (KV head,
+// sequence), so that the 512 KiB a head's ring holds stream through that many CUs: one CU
+// alone reached only ~37 B/clk of it.  Every workgroup computes cos / sin of p * omega_i;
+// the one whose slots hold p mod 512 rotates the new key by the token's position p and
+// writes K and V to that slot (the same bits as the rotating append), and only it reads
+// that slot.  Each workgroup attends query heads 4 kvh .. 4 kvh + 3 over its filled slots
+// (one 32-key step per wave), merges its two waves through LDS and publishes the partial
+// (reference max, sum, unnormalised o) to the workspace.  The last workgroup to arrive
+// (a counter per (KV head, sequence), which it resets to zero) merges the kRingSplits
+// partials by log-sum-exp, normalises, gates and stores as the combine does.
+// [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
+// tokens); [T3] "Sliding window 512" (RoPE theta 1e4 over all 256 dims).
+__global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
+    const bf16_t* __restrict__ v_new, bf16_t* __restrict__ k_ring, bf16_t* __restrict__ v_ring,
+    const int* __restrict__ pos, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
+    float* __restrict__ lse, RopeTable tab, float sl2, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml, unsigned* __restrict__ counters) {
+  constexpr int kHalf = 128;       // rot_dim / 2
+  __shared__ f32x2 cs[kHalf];
+  __shared__ __attribute__((aligned(16))) float p_lds[kSplitWaves][kStep][4];
+  __shared__ __attribute__((aligned(16))) float part_o[kSplitWaves][kGroup][kD];
+  __shared__ float part_ml[kSplitWaves][kGroup][2];
+  __shared__ unsigned last;
+
+  const int kvh = blockIdx.x / kRingSplits, sp = blockIdx.x % kRingSplits, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int half = lane >> 5, dg = lane & 31;
+  const int p = pos[b];
+  // Merge threads: head hl, dims d0 .. d0 + 7.
+  const int hl = tid >> 5, d0 = 8 * (tid & 31);
+  const long long row = (long long)b * kHq + kvh * kGroup + hl;
+  const float gate_logit = bf16_to_f32(gate[row]);
+
+  const bool qlane = n16 < kGroup;
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = q + ((long long)b * kHq + kvh * kGroup + (qlane ? n16 : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+  }
+
+  static_assert(64 * kSplitWaves >= kHalf, "one thread per frequency");
+  if (tid < kHalf) {
+    float sv, cv;
+    sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
+    cs[tid] = f32x2{cv, sv};
+  }
+  __syncthreads();
+
+  const long long ring_off = ((long long)b * kRingSlots * kHkv + kvh) * kD;
+  const int slot_new = p & (kRingSlots - 1);
+  if (p >= 0 && slot_new / kRingPerSplit == sp) {
+    const long long dst = ring_off + (long long)slot_new * kHkv * kD;
+    const long long src = ((long long)b * kHkv + kvh) * kD;
+    if (tid < kHalf / 8) {
+      // Dims d0 .. d0 + 7 and their partners d0 + 128 .. d0 + 135.
+      const int d = 8 * tid;
+      const uint4 xa = *reinterpret_cast<const uint4*>(k_new + src + d);
+      const uint4 xb = *reinterpret_cast<const uint4*>(k_new + src + d + kHalf);
+      const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
+      const uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
+      uint32_t ya[4], yb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 c0 = cs[d + 2 * e], c1 = cs[d + 2 * e + 1];
+        float ya0, yb0, ya1, yb1;
+        rope_pair(bf16_lo(wa[e]), bf16_lo(wb[e]), c0.x, c0.y, &ya0, &yb0);
+        rope_pair(bf16_hi(wa[e]), bf16_hi(wb[e]), c1.x, c1.y, &ya1, &yb1);
+        ya[e] = pack_bf16x2(ya0, ya1);
+        yb[e] = pack_bf16x2(yb0, yb1);
+      }
+      *reinterpret_cast<uint4*>(k_ring + dst + d) = uint4{ya[0], ya[1], ya[2], ya[3]};
+      *reinterpret_cast<uint4*>(k_ring + dst + d + kHalf) = uint4{yb[0], yb[1], yb[2], yb[3]};
+    } else if (tid < kHalf / 8 + kD / 8) {
+      const int d = 8 * (tid - kHalf / 8);
+      *reinterpret_cast<uint4*>(v_ring + dst + d) = *reinterpret_cast<const uint4*>(v_new + src + d);
+    }
+    // The new row is read below by this workgroup only: the barrier's workgroup-scope
+    // release and acquire make it visible (its waves share one CU).
+    __syncthreads();
+  }
+
+  // Q^T operand as in the split kernel (loaded first, above), rotated with the shared table.
+  if (qlane) {
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      const bf16x8 xa = qf[dc], xb = qf[dc + 4];
+      f32x4 ya0, ya1, yb0, yb1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x2 c = cs[32 * dc + 8 * g + e];
+        float ya, yb;
+        rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
+        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
+      }
+      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
+      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
+      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      qf[dc + 4] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    }
+  }
+
+  // Slots [k_begin, k_end) of this wave: the ring's first min(p + 1, 512) slots are filled
+  // (formed without p + 1, which overflows at the largest position).
+  const int kv_len = p >= 0 ? min(p, kRingSlots - 1) + 1 : 0;
+  const int k_begin = kRingPerSplit * sp + kStep * w;
+  const int k_end = min(kv_len, k_begin + kStep);
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[kGroup][8];
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  attend_keys(qf, k_ring + ring_off, v_ring + ring_off, k_begin, k_end, sl2, p_lds[w], lane,
+              m_run, l_run, o);
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], 32);
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      *reinterpret_cast<f32x4*>(&part_o[w][h][8 * dg]) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+      *reinterpret_cast<f32x4*>(&part_o[w][h][8 * dg + 4]) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+    }
+  }
+  if (lane < kGroup) {
+    part_ml[w][lane][0] = m_run;
+    part_ml[w][lane][1] = l_run;
+  }
+  __syncthreads();
+
+  // This workgroup's partial: its waves merged under their largest reference max.
+  const long long part = ((long long)(b * kHkv + kvh) * kRingSplits + sp) * kGroup + hl;
+  {
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kSplitWaves; ++v) M = fmaxf(M, part_ml[v][hl][0]);
+    const float M_use = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    f32x4 a0 = f32x4{}, a1 = f32x4{};
+#pragma unroll
+    for (int v = 0; v < kSplitWaves; ++v) {
+      const float wgt = fast_exp2(part_ml[v][hl][0] - M_use);
+      L += part_ml[v][hl][1] * wgt;
+      a0 += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d0]) * wgt;
+      a1 += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d0 + 4]) * wgt;
+    }
+    *reinterpret_cast<f32x4*>(ws_o + part * kD + d0) = a0;
+    *reinterpret_cast<f32x4*>(ws_o + part * kD + d0 + 4) = a1;
+    if ((tid & 31) == 0) {
+      ws_ml[2 * part] = M;
+      ws_ml[2 * part + 1] = L;
+    }
+  }
+  // Publish the partial (device-scope release), then count this workgroup in; the last one
+  // of the (KV head, sequence) merges.
+  __threadfence();
+  __syncthreads();
+  unsigned* counter = counters + b * kHkv + kvh;
+  if (tid == 0) last = atomicAdd(counter, 1u) == kRingSplits - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // acquire: every other workgroup's partial is visible
+
+  const long long part0 = ((long long)(b * kHkv + kvh) * kRingSplits) * kGroup + hl;
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kRingSplits; ++s) M = fmaxf(M, ws_ml[2 * (part0 + s * kGroup)]);
+  const float M_use = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  f32x4 a0 = f32x4{}, a1 = f32x4{};
+#pragma unroll
+  for (int s = 0; s < kRingSplits; ++s) {
+    const long long ps = part0 + s * kGroup;
+    const float wgt = fast_exp2(ws_ml[2 * ps] - M_use);
+    L += ws_ml[2 * ps + 1] * wgt;
+    a0 += *reinterpret_cast<const f32x4*>(ws_o + ps * kD + d0) * wgt;
+    a1 += *reinterpret_cast<const f32x4*>(ws_o + ps * kD + d0 + 4) * wgt;
+  }
+  const float sg = 1.f / (1.f + expf(-gate_logit));
+  const float f = L > 0.f ? sg / L : 0.f;
+  *reinterpret_cast<uint4*>(out + row * kD + d0) =
+      uint4{pack_bf16x2(a0[0] * f, a0[1] * f), pack_bf16x2(a0[2] * f, a0[3] * f),
+            pack_bf16x2(a1[0] * f, a1[1] * f), pack_bf16x2(a1[2] * f, a1[3] * f)};
+  if ((tid & 31) == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (tid == 0) *counter = 0u;  // ready for the next step (kernel boundaries order it)
+}
+
+// Clears n 32-bit counters (a kernel, not a memset, so that it can sit in a captured graph).
+__global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
 
 DecodePlan decode_plan(int B, int max_keys) {
@@ -773,12 +982,42 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
   return hipGetLastError();
 }
 
+size_t ring_step_workspace_bytes(int B) {
+  if (B > kRingSplitMaxB) return 0;  // the fused kernel needs none
+  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
+  return parts * (kD + 2) * sizeof(float) + (size_t)B * kHkv * sizeof(unsigned);
+}
+
+hipError_t clear_ring_counters(void* workspace, int B, hipStream_t stream) {
+  if (B > kRingSplitMaxB) return hipSuccess;
+  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
+  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<float*>(workspace) + parts * (kD + 2));
+  const int n = B * kHkv;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     counters, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
                             bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,
                             const bf16_t* gate, bf16_t* out, float* lse, const RopeTable& tab,
-                            float scale_log2e, hipStream_t stream) {
-  hipLaunchKernelGGL(ring_step_kernel, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves), 0, stream, q, k_new,
-                     v_new, k_ring, v_ring, pos, gate, out, lse, tab, scale_log2e);
+                            float scale_log2e, void* workspace, hipStream_t stream) {
+  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o + parts * kD;
+  unsigned* counters = reinterpret_cast<unsigned*>(ws_ml + parts * 2);
+  // Split for B <= 2 only: each split workgroup's device-scope fence (an L2 write-back and
+  // invalidate) grows with the workgroup count.  Measured per step through the driver:
+  // B = 1 10.4 us split against 16.8 fused, B = 2 13.4 against 17.0, B = 4 19.6 against 17.2.
+  if (B <= kRingSplitMaxB) {
+    hipLaunchKernelGGL(ring_split_kernel, dim3(kHkv * kRingSplits, (unsigned)B),
+                       dim3(64 * kSplitWaves), 0, stream, q, k_new, v_new, k_ring, v_ring, pos,
+                       gate, out, lse, tab, scale_log2e, ws_o, ws_ml, counters);
+  } else {
+    hipLaunchKernelGGL(ring_step_kernel, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves), 0,
+                       stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out, lse, tab,
+                       scale_log2e);
+  }
   return hipGetLastError();
 }
 

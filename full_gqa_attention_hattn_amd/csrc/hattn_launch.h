@@ -65,11 +65,17 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
 // One decode step of a sliding layer in one launch: rotate K by pos and append K / V at
 // ring slot pos mod 512 of k_ring / v_ring [B, 512, 4, 256], then attend (Q-RoPE fused),
 // gate and store out [B, 1, 16, 256] (and lse [B, 1, 16] unless null).  q, k_new, v_new
-// are the token's un-rotated projections [B, 1, *, 256].  No workspace.
+// are the token's un-rotated projections [B, 1, *, 256].  For B <= 2 the ring is split
+// over 8 workgroups per (sequence, KV head), and workspace (16-byte aligned, at least
+// ring_step_workspace_bytes(B) bytes) holds their partials and one counter per (sequence,
+// KV head), which must be zero before the first step (clear_ring_counters) and which every
+// step leaves at zero; larger batches use one workgroup each and no workspace.
+size_t ring_step_workspace_bytes(int B);
+hipError_t clear_ring_counters(void* workspace, int B, hipStream_t stream);
 hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
                             bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,
                             const bf16_t* gate, bf16_t* out, float* lse, const RopeTable& tab,
-                            float scale_log2e, hipStream_t stream);
+                            float scale_log2e, void* workspace, hipStream_t stream);
 
 // 8-bit KV decode: caches [B, cap, 4, 256] E4M3 codes, scales [B, 4, cap] fp32; same plan
 // and workspace as launch_decode.

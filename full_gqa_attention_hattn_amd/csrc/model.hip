@@ -47,6 +47,15 @@ hattn_status check_common(const hattn_layer_io* layers, int32_t n_layers, int32_
   return HATTN_OK;
 }
 
+// Decode workspace layout: the full layers' split partials, then (16-byte aligned) the
+// sliding layers' ring-step partials and counters.
+size_t full_region_bytes(int32_t n_layers, int32_t B, int32_t cap) {
+  hattn_layer_cfg full;
+  hattn_cfg_preset(HATTN_FULL, &full);
+  const size_t need = n_layers > 3 ? hattn_decode_workspace_bytes(&full, B, cap) : 0;
+  return (need + 15) & ~(size_t)15;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,13 +78,8 @@ hattn_status hattn_model_kv_bytes(int32_t n_layers, int32_t B, int32_t cap, size
 }
 
 size_t hattn_model_decode_workspace_bytes(int32_t n_layers, int32_t B, int32_t cap) {
-  if (n_layers < 1 || n_layers > kMaxLayers || B < 1 || cap < kRing) return 0;
-  hattn_layer_cfg full, sliding;
-  hattn_cfg_preset(HATTN_FULL, &full);
-  hattn_cfg_preset(HATTN_SLIDING, &sliding);
-  size_t need = n_layers > 3 ? hattn_decode_workspace_bytes(&full, B, cap) : 0;
-  const size_t s = hattn_decode_workspace_bytes(&sliding, B, kRing);
-  return need > s ? need : s;
+  if (n_layers < 1 || n_layers > kMaxLayers || B < 1 || B > 65535 || cap < kRing) return 0;
+  return full_region_bytes(n_layers, B, cap) + hattn::ring_step_workspace_bytes(B);
 }
 
 hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, int32_t cap,
@@ -94,6 +98,11 @@ hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, 
   hattn_cfg_preset(HATTN_SLIDING, &sliding);
   const hattn::RopeTable sliding_tab = hattn::rope_table(&sliding);
   const float sliding_scale = hattn::scale_log2e(&sliding);
+  void* ring_ws = static_cast<char*>(workspace) + full_region_bytes(n_layers, B, cap);
+  {
+    const hipError_t e = hattn::clear_ring_counters(ring_ws, B, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hattn::note_hip_error(e);
+  }
   for (int32_t l = 0; l < n_layers; ++l) {
     const hattn_layer_io& L = layers[l];
     hattn_layer_cfg cfg;
@@ -105,7 +114,7 @@ hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, 
           static_cast<const hattn::bf16_t*>(L.v), static_cast<hattn::bf16_t*>(L.k_cache),
           static_cast<hattn::bf16_t*>(L.v_cache), pos, B,
           static_cast<const hattn::bf16_t*>(L.gate), static_cast<hattn::bf16_t*>(L.out),
-          static_cast<float*>(L.lse), sliding_tab, sliding_scale,
+          static_cast<float*>(L.lse), sliding_tab, sliding_scale, ring_ws,
           reinterpret_cast<hipStream_t>(stream));
       if (e != hipSuccess) return hattn::note_hip_error(e);
       continue;
