@@ -252,12 +252,18 @@ typedef struct hattn_layer_io {
   float* lse;
 } hattn_layer_io;
 
-/* Device workspace hattn_model_decode needs (0 for invalid sizes). */
+/* Device workspace hattn_model_decode needs (0 for invalid sizes): the full layers' split
+ * partials and, for B <= 2, the sliding layers' ring partials and per-head counters.  Its
+ * contents between calls do not matter: each call clears the counters (with a kernel) before
+ * its first sliding layer. */
 size_t hattn_model_decode_workspace_bytes(int32_t n_layers, int32_t B, int32_t cap);
 
 /* One decode step of every layer, in layer order, on `stream`: for each layer the new
  * token at pos[b] (int32 [B], device) is rotated and appended (hattn_kv_append_rope) and
- * attended (hattn_decode with HATTN_ROPE_Q_FUSED).  layers: host array of n_layers.
+ * attended (hattn_decode with HATTN_ROPE_Q_FUSED); a sliding layer does both in one launch
+ * (the same arithmetic).  layers: host array of n_layers.  workspace: device, 16-byte
+ * aligned, at least hattn_model_decode_workspace_bytes(n_layers, B, cap) bytes; calls
+ * that overlap on one workspace race.
  * Nothing is allocated and no input is modified, so a captured step replays exactly.
  * All pointers are checked before anything is enqueued; a later non-OK status can only
  * be HATTN_ERR_HIP.  Errors: those of the per-layer calls, HATTN_ERR_WORKSPACE, and
