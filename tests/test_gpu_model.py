@@ -118,17 +118,19 @@ def test_model_prefill_chunks_then_decode(h):
             check_outputs(outs[l][b], lses[l][b], y, lse, f"model layer {l} ({kind}) b={b}")
 
 
-def test_model_decode_graph_replay(h):
+@pytest.mark.parametrize("positions", [[1000], [5, 1000, 2000]])
+def test_model_decode_graph_replay(h, positions):
     """A captured decode step of a 4-layer schedule replays to the eager result, several
-    times, with other work and synchronisations in between."""
-    say("model decode graph replay")
-    n_layers, B, cap = 4, 3, 2048
+    times, with other work and synchronisations in between.  B = 1 takes the split ring
+    step (its counters cleared by a kernel in the graph), B = 3 the fused one."""
+    say(f"model decode graph replay B={len(positions)}")
+    n_layers, B, cap = 4, len(positions), 2048
     layers = _model_layers(h, n_layers, B, 1, cap, 161)
     for l, L in enumerate(layers):      # history: random rotated keys at every slot
         hist = synth.cache_inputs(162, B, L["k_cache"].shape[1], L["k_cache"].shape[1], "cuda", layer=l)
         L["k_cache"].copy_(hist["cache_k"])
         L["v_cache"].copy_(hist["cache_v"])
-    pos = synth.positions([5, 1000, 2000], B, "cuda")
+    pos = synth.positions(positions, B, "cuda")
     ws = torch.empty(h.model_decode_workspace_bytes(n_layers, B, cap), dtype=torch.uint8, device="cuda")
     h.model_decode(layers, cap, pos, ws)
     torch.cuda.synchronize()
@@ -153,7 +155,7 @@ def test_model_decode_graph_replay(h):
             assert torch.equal(L["lse"], ref[l][1]), (rep, l)
         del junk
     # and the eager result matches the oracle
-    p = [5, 1000, 2000]
+    p = positions
     for l, L in enumerate(layers):
         kind = L["kind"]
         for b in range(B):
