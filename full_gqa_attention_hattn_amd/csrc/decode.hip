@@ -525,13 +525,26 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   const float M_use = M == -INFINITY ? 0.f : M;
 
+  // Eight chunks per batch, their loads issued before any of their arithmetic (indices
+  // past the last chunk read the last one and get weight 0), so that a thread has 24 loads
+  // in flight: the loop is bound by load latency, not bandwidth.
+  constexpr int kBatch = 8;
   float L = 0.f, acc = 0.f;
-#pragma unroll 4
-  for (int c = cg; c < nchunks; c += kCombGroups) {
-    const long long pc = (base + c) * kGroup + hl;
-    const float wgt = fast_exp2(ws_ml[pc * 2] - M_use);
-    L += ws_ml[pc * 2 + 1] * wgt;
-    acc += ws_o[pc * kD + d] * wgt;
+  for (int c0 = cg; c0 < nchunks; c0 += kBatch * kCombGroups) {
+    float mv[kBatch], lv[kBatch], ov[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const long long pc = (base + min(c0 + u * kCombGroups, nchunks - 1)) * kGroup + hl;
+      mv[u] = ws_ml[pc * 2];
+      lv[u] = ws_ml[pc * 2 + 1];
+      ov[u] = ws_o[pc * kD + d];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float wgt = c0 + u * kCombGroups < nchunks ? fast_exp2(mv[u] - M_use) : 0.f;
+      L += lv[u] * wgt;
+      acc += ov[u] * wgt;
+    }
   }
   red_o[cg][dl] = acc;
   if (dl == 0) red_l[cg] = L;
