@@ -68,6 +68,17 @@ int decode_max_keys(const hattn_layer_cfg* cfg, int32_t cap) {
   return cfg->kind == HATTN_SLIDING ? cfg->window : cap;
 }
 
+// Workspace a decode needs: the split partials, or for a sliding layer at small B the ring
+// split's partials and counters (whichever is larger, so one size serves both).
+size_t decode_need(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
+  size_t need = hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));
+  if (cfg->kind == HATTN_SLIDING && hattn::ring_decode_applies(B)) {
+    const size_t r = hattn::ring_step_workspace_bytes(B);
+    need = need > r ? need : r;
+  }
+  return need;
+}
+
 }  // namespace
 
 namespace hattn {
@@ -274,7 +285,7 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
   if (check_cfg(cfg) != HATTN_OK || B < 0 || cap < 1) return 0;
   if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return 0;
   if (B == 0) return 0;
-  return hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));
+  return decode_need(cfg, B, cap);
 }
 
 hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
@@ -293,10 +304,16 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
     return HATTN_ERR_ALIGN;
   if (B > 65535 || (long long)B * cap >= (1LL << 40)) return HATTN_ERR_SHAPE;
   const hattn::DecodePlan plan = hattn::decode_plan(B, decode_max_keys(cfg, cap));
-  const size_t need = hattn::decode_workspace_bytes(B, plan);
+  const size_t need = decode_need(cfg, B, cap);
   if (workspace == nullptr || workspace_bytes < need) return HATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
   const hattn::RopeTable tab = rope_table(cfg);
+  if (cfg->kind == HATTN_SLIDING && hattn::ring_decode_applies(B))
+    return hip_status(hattn::launch_ring_decode(
+        static_cast<const hattn::bf16_t*>(q), static_cast<const hattn::bf16_t*>(k_cache),
+        static_cast<const hattn::bf16_t*>(v_cache), pos, B,
+        static_cast<const hattn::bf16_t*>(gate), static_cast<hattn::bf16_t*>(out), lse,
+        (flags & HATTN_ROPE_Q_FUSED) != 0, tab, scale_log2e(cfg), workspace, as_stream(stream)));
   return hip_status(hattn::launch_decode(
       static_cast<const hattn::bf16_t*>(q), static_cast<const hattn::bf16_t*>(k_cache),
       static_cast<const hattn::bf16_t*>(v_cache), cap, pos, B,

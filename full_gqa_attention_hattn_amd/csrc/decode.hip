@@ -738,12 +738,16 @@ static_assert(kRingPerSplit == kSplitWaves * kStep, "one 32-key step per wave");
 // partials by log-sum-exp, normalises, gates and stores as the combine does.
 // [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
 // tokens); [T3] "Sliding window 512" (RoPE theta 1e4 over all 256 dims).
+// kAppend: the step's append is fused in (the schedule driver); otherwise the token's key
+// and value are already in the ring (a plain sliding decode), and rope_q says whether q
+// still needs its rotation.
+template <bool kAppend>
 __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
     const bf16_t* __restrict__ v_new, bf16_t* __restrict__ k_ring, bf16_t* __restrict__ v_ring,
     const int* __restrict__ pos, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
     float* __restrict__ lse, RopeTable tab, float sl2, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml, unsigned* __restrict__ counters) {
+    float* __restrict__ ws_ml, unsigned* __restrict__ counters, int rope_q) {
   constexpr int kHalf = 128;       // rot_dim / 2
   __shared__ f32x2 cs[kHalf];
   __shared__ __attribute__((aligned(16))) float p_lds[kSplitWaves][kStep][4];
@@ -771,7 +775,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
   }
 
   static_assert(64 * kSplitWaves >= kHalf, "one thread per frequency");
-  if (tid < kHalf) {
+  if (tid < kHalf && (kAppend || rope_q)) {
     float sv, cv;
     sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
     cs[tid] = f32x2{cv, sv};
@@ -780,7 +784,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
 
   const long long ring_off = ((long long)b * kRingSlots * kHkv + kvh) * kD;
   const int slot_new = p & (kRingSlots - 1);
-  if (p >= 0 && slot_new / kRingPerSplit == sp) {
+  if (kAppend && p >= 0 && slot_new / kRingPerSplit == sp) {
     const long long dst = ring_off + (long long)slot_new * kHkv * kD;
     const long long src = ((long long)b * kHkv + kvh) * kD;
     if (tid < kHalf / 8) {
@@ -812,7 +816,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
   }
 
   // Q^T operand as in the split kernel (loaded first, above), rotated with the shared table.
-  if (qlane) {
+  if (qlane && rope_q) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       const bf16x8 xa = qf[dc], xb = qf[dc + 4];
@@ -1023,9 +1027,9 @@ hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* 
   // invalidate) grows with the workgroup count.  Measured per step through the driver:
   // B = 1 10.4 us split against 16.8 fused, B = 2 13.4 against 17.0, B = 4 19.6 against 17.2.
   if (B <= kRingSplitMaxB) {
-    hipLaunchKernelGGL(ring_split_kernel, dim3(kHkv * kRingSplits, (unsigned)B),
+    hipLaunchKernelGGL(ring_split_kernel<true>, dim3(kHkv * kRingSplits, (unsigned)B),
                        dim3(64 * kSplitWaves), 0, stream, q, k_new, v_new, k_ring, v_ring, pos,
-                       gate, out, lse, tab, scale_log2e, ws_o, ws_ml, counters);
+                       gate, out, lse, tab, scale_log2e, ws_o, ws_ml, counters, 1);
   } else {
     hipLaunchKernelGGL(ring_step_kernel, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves), 0,
                        stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out, lse, tab,
@@ -1033,5 +1037,26 @@ hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* 
   }
   return hipGetLastError();
 }
+
+hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_t* v_ring,
+                              const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
+                              bool rope_q, const RopeTable& tab, float scale_log2e,
+                              void* workspace, hipStream_t stream) {
+  if (B > kRingSplitMaxB) return hipErrorInvalidValue;
+  const hipError_t e = clear_ring_counters(workspace, B, stream);
+  if (e != hipSuccess) return e;
+  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o + parts * kD;
+  unsigned* counters = reinterpret_cast<unsigned*>(ws_ml + parts * 2);
+  // The ring is only read (k_new / v_new unused without the append).
+  hipLaunchKernelGGL(ring_split_kernel<false>, dim3(kHkv * kRingSplits, (unsigned)B),
+                     dim3(64 * kSplitWaves), 0, stream, q, nullptr, nullptr,
+                     const_cast<bf16_t*>(k_ring), const_cast<bf16_t*>(v_ring), pos, gate, out,
+                     lse, tab, scale_log2e, ws_o, ws_ml, counters, rope_q ? 1 : 0);
+  return hipGetLastError();
+}
+
+bool ring_decode_applies(int B) { return B <= kRingSplitMaxB; }
 
 }  // namespace hattn

@@ -71,6 +71,14 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
 // KV head), which must be zero before the first step (clear_ring_counters) and which every
 // step leaves at zero; larger batches use one workgroup each and no workspace.
 size_t ring_step_workspace_bytes(int B);
+// The same split attention for a plain sliding decode (the token's key and value already in
+// the ring; q rotated unless rope_q), for B with ring_decode_applies(B): clears the counters
+// and launches, in that order, on `stream`.
+bool ring_decode_applies(int B);
+hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_t* v_ring,
+                              const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
+                              bool rope_q, const RopeTable& tab, float scale_log2e,
+                              void* workspace, hipStream_t stream);
 hipError_t clear_ring_counters(void* workspace, int B, hipStream_t stream);
 hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
                             bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,

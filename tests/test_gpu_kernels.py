@@ -250,12 +250,16 @@ def test_decode_full_cache(h, fused):
     _decode_case(h, "full", [0, 31, 777, 1999, 4999], 5000, 71, fused)
 
 
+@pytest.mark.parametrize("positions", [
+    [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9, (1 << 31) - 1],  # split + combine
+    [131072],                                # B = 1 and 2: the ring split in one launch
+    [300, (1 << 31) - 1],
+])
 @pytest.mark.parametrize("fused", [True, False])
-def test_decode_ring(h, fused):
-    say(f"decode ring fused={fused}")
+def test_decode_ring(h, fused, positions):
+    say(f"decode ring fused={fused} B={len(positions)}")
     # up to the largest int32 position, where p + 1 would overflow
-    _decode_case(h, "sliding", [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9,
-                                (1 << 31) - 1], 512, 81, fused)
+    _decode_case(h, "sliding", positions, 512, 81, fused)
 
 
 def test_decode_equals_prefill_row(h):
