@@ -234,6 +234,13 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   const int wt_lo = kSliding ? max(0, Pw0 - (window - 1)) / kBN : 0;
   const int wt_hi = min(Pwl, capk - 1) / kBN;
 
+  // The cos/sin table's column is tid mod kHalf on every pass, so each thread needs one
+  // frequency.  It is read before the Q rows: loads complete in issue order, and behind
+  // them its wait would also wait for all of Q.
+  static_assert(kThreads % kHalf == 0, "a thread keeps one table column");
+  const int fcol = tid & (kHalf - 1);
+  const float freq = rope_q ? tab.inv_freq[fcol] : 0.f;
+
   // Q^T operand: lane (n, hh) holds dims 16dc + 8hh .. +7 of query row n of this wave.
   bf16x8 qf[16];
   {
@@ -246,11 +253,10 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 
   if (rope_q) {
     f32x2* cs = reinterpret_cast<f32x2*>(smem);
-    for (int e = tid; e < kBQ * kHalf; e += kThreads) {
-      const int r = e / kHalf, f = e - r * kHalf;
+    for (int r = tid / kHalf; r < kBQ; r += kThreads / kHalf) {
       float sv, cv;
-      sincos_angle(rope_angle(P0 + r, tab.inv_freq[f]), &sv, &cv);
-      cs[r * kPitch + f] = f32x2{cv, sv};
+      sincos_angle(rope_angle(P0 + r, freq), &sv, &cv);
+      cs[r * kPitch + fcol] = f32x2{cv, sv};
     }
     __syncthreads();
 #pragma unroll
