@@ -164,7 +164,8 @@ hattn_status hattn_prefill_ring(const hattn_layer_cfg* cfg, const void* q, const
                                 void* out, float* lse, uint32_t flags, void* stream);
 
 /* Bytes of device workspace hattn_decode needs for B sequences and this cache capacity
- * (its split-KV partial results).  0 for an invalid configuration. */
+ * (its split-KV partial results; for a sliding layer at B <= 2 also its arrival
+ * counters).  0 for an invalid configuration. */
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap);
 
 /* Single-token decode.  q [B,1,16,256] (rotated unless flags & HATTN_ROPE_Q_FUSED),
@@ -175,7 +176,11 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
  *            min(pos[b] + 1, window) slots are valid (the ring is filled in position
  *            order from position 0), and every valid slot is visible.
  * Same arithmetic as hattn_prefill.  The key range is split into chunks whose partial
- * (max, sum, output) triples are merged by log-sum-exp in a second kernel.
+ * (max, sum, output) triples are merged by log-sum-exp in a second kernel.  A sliding
+ * layer at B <= 2 runs as one kernel instead: 8 workgroups per (sequence, KV head) each
+ * take 64 ring slots, and the last of them to finish merges the 8 partials.  Its arrival
+ * counters live in the workspace and the call clears them first, so calls that share a
+ * workspace must be ordered (one stream); they race otherwise.
  * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes.
  * B <= 65535 (one grid row per sequence), else HATTN_ERR_SHAPE.
  * [T2] "The real bottleneck of a million-token context" (the ring keeps the last 512
