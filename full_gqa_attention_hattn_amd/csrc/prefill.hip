@@ -460,20 +460,41 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   float l_a, l_b;
   halves(l_run, &l_a, &l_b);
   const float l_tot = l_a + l_b;
+  // row_i is a valid row in every lane (clamped above), so all lanes take part in the
+  // exchange below; only rows that exist are stored.
+  const long long row = (long long)b * Sq + row_i;
+  const float g = bf16_to_f32(gate[row * kHq + h]);
+  const float sg = 1.f / (1.f + expf(-g));
+  const float f = l_tot > 0.f ? sg / l_tot : 0.f;
+  // O^T accumulator element 4i + j of block mb is dim 32mb + 8i + 4hh + j: a lane holds
+  // 4-dim pieces of its row.  v_permlane32_swap trades pieces between the lanes hh = 0 and
+  // hh = 1 of one row (lanes n and n + 32): for each pair of pieces (i = 2ip, 2ip + 1) the
+  // hh = 1 lane hands over its piece 2ip and the hh = 0 lane its piece 2ip + 1, so lane
+  // hh = 0 ends with dims 16ip + 0..7 and lane hh = 1 with dims 16ip + 8..15 of the block,
+  // 16 contiguous bytes each.
+  uint4 ov[8][2];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+    for (int ip = 0; ip < 2; ++ip) {
+      const int e = 8 * ip;  // piece 2ip starts at accumulator element 8ip
+      const uint32_t a0 = pack_bf16x2(o[mb][e] * f, o[mb][e + 1] * f);
+      const uint32_t a1 = pack_bf16x2(o[mb][e + 2] * f, o[mb][e + 3] * f);
+      const uint32_t c0 = pack_bf16x2(o[mb][e + 4] * f, o[mb][e + 5] * f);
+      const uint32_t c1 = pack_bf16x2(o[mb][e + 6] * f, o[mb][e + 7] * f);
+      // Upper lanes of the first operand trade with lower lanes of the second.
+      const auto s0 = __builtin_amdgcn_permlane32_swap(a0, c0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(a1, c1, false, false);
+      ov[mb][ip] = uint4{s0[0], s1[0], s0[1], s1[1]};
+    }
+  }
   if (row_ok) {
-    const long long row = (long long)b * Sq + row_i;
-    const float g = bf16_to_f32(gate[row * kHq + h]);
-    const float sg = 1.f / (1.f + expf(-g));
-    const float f = l_tot > 0.f ? sg / l_tot : 0.f;
-    bf16_t* orow = out + (row * kHq + h) * kD + 4 * hh;
-    // O^T accumulator element 4i + j of block mb is dim 32mb + 8i + 4hh + j.
+    bf16_t* orow = out + (row * kHq + h) * kD + 8 * hh;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint2 v{pack_bf16x2(o[mb][4 * i] * f, o[mb][4 * i + 1] * f),
-                      pack_bf16x2(o[mb][4 * i + 2] * f, o[mb][4 * i + 3] * f)};
-        *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * i) = v;
+      for (int ip = 0; ip < 2; ++ip) {
+        *reinterpret_cast<uint4*>(orow + 32 * mb + 16 * ip) = ov[mb][ip];
       }
     }
     if (lse != nullptr && hh == 0) {
