@@ -292,17 +292,29 @@ __global__ __launch_bounds__(S::kThreads) void proj_kernel(
   wait_vm<0>();  // no copy may still be writing this workgroup's LDS when it exits
 
   // acc[a][b] element 4i + j: feature 32 kAN wn + 32a + 8i + 4hk + j, token
-  // 32 kAT wt + 32b + r32.  Each run of 4 features goes to q, k, v, the gate logits or Y.
+  // 32 kAT wt + 32b + r32.  The lanes hk = 0 and 1 of a token (r32 and r32 + 32) hold
+  // alternate 4-feature pieces; v_permlane32_swap trades one piece of each pair (i = 2ip,
+  // 2ip + 1) between them, so lane hk ends with features 16ip + 8hk .. + 7 of the block and
+  // stores 16 contiguous bytes.  Each run of 8 features goes to q, k, v, the gate logits or
+  // Y (N and the q/k/v/gate boundaries are multiples of 8).
 #pragma unroll
   for (int b = 0; b < kAT; ++b) {
     const int t = t_tile + 32 * kAT * wt + 32 * b + r32;
-    if (t >= T) continue;
 #pragma unroll
     for (int a = 0; a < kAN; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = n_tile + 32 * kAN * wn + 32 * a + 8 * i + 4 * hk;
-        if (f >= N) continue;
+      for (int ip = 0; ip < 2; ++ip) {
+        const int e = 8 * ip;
+        const uint32_t a0 = pack_bf16x2(acc[a][b][e], acc[a][b][e + 1]);
+        const uint32_t a1 = pack_bf16x2(acc[a][b][e + 2], acc[a][b][e + 3]);
+        const uint32_t c0 = pack_bf16x2(acc[a][b][e + 4], acc[a][b][e + 5]);
+        const uint32_t c1 = pack_bf16x2(acc[a][b][e + 6], acc[a][b][e + 7]);
+        // Upper lanes of the first operand trade with lower lanes of the second (all lanes
+        // take part; only valid tokens and features are stored).
+        const auto s0 = __builtin_amdgcn_permlane32_swap(a0, c0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(a1, c1, false, false);
+        const int f = n_tile + 32 * kAN * wn + 32 * a + 16 * ip + 8 * hk;
+        if (t >= T || f >= N) continue;
         bf16_t* dst = y0;
         int col = f, ld = N;
         if (kFused) {
@@ -311,9 +323,8 @@ __global__ __launch_bounds__(S::kThreads) void proj_kernel(
           else if (f < kQkvDim) { dst = y2; col = f - kQDim - kKvDim; ld = kKvDim; }
           else { dst = y3; col = f - kQkvDim; ld = kGateRows; }
         }
-        const uint2 v{pack_bf16x2(acc[a][b][4 * i], acc[a][b][4 * i + 1]),
-                      pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3])};
-        *reinterpret_cast<uint2*>(dst + (long long)t * ld + col) = v;
+        *reinterpret_cast<uint4*>(dst + (long long)t * ld + col) =
+            uint4{s0[0], s1[0], s0[1], s1[1]};
       }
   }
 }
@@ -446,6 +457,7 @@ template <int kFused, class S>
 hipError_t launch_tiles(const bf16_t* x, int T, int K, const bf16_t* w, const bf16_t* w_gate,
                         int N, bf16_t* y0, bf16_t* y1, bf16_t* y2, bf16_t* y3,
                         hipStream_t stream) {
+  if (N % 8 != 0) return hipErrorInvalidValue;  // the epilogue stores runs of 8 features
   const int nN = (N + S::kTN - 1) / S::kTN, nT = (T + S::kTT - 1) / S::kTT;
   const int gN = xcd_split(nN, nT, S::kTN, S::kTT, K);
   hipLaunchKernelGGL((proj_kernel<kFused, S>), dim3((unsigned)grid_size(nN, nT, gN)),
