@@ -21,12 +21,50 @@ constexpr int kRopeThreads = 256;
 // One workgroup rotates kRopeTokens consecutive tokens (flattened b*S + s).  The cos/sin
 // of each (token, frequency) is computed once into LDS and shared by the 16 query heads
 // and 4 key heads.  Each work item turns 8 pairs: 16 bytes at d and 16 bytes at d + r/2.
+// Work items cover only the heads present (K alone when q is null, and so on).
+
+// Row and first dim of work item e; null when its token is past the end.
+__device__ __forceinline__ bf16_t* rope_item(bf16_t* q, bf16_t* k, long long tok0,
+                                             long long ntok, int e, int h_lo, int groups,
+                                             int per_tok, int* t_out, int* d0_out) {
+  const int t = e / per_tok;
+  const int rem = e - t * per_tok;
+  const int hh = h_lo + rem / groups, gi = rem - (hh - h_lo) * groups;
+  const long long tok = tok0 + t;
+  *t_out = t;
+  *d0_out = gi * 8;
+  if (tok >= ntok) return nullptr;
+  return hh < kHq ? q + (tok * kHq + hh) * kD : k + (tok * kHkv + (hh - kHq)) * kD;
+}
+
 __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(
     bf16_t* __restrict__ q, bf16_t* __restrict__ k, const int* __restrict__ pos0, int S,
     long long ntok, RopeTable tab) {
   __shared__ f32x2 cs[kRopeTokens][kMaxHalfRot];
   const int half = tab.rot_dim >> 1;
   const long long tok0 = (long long)blockIdx.x * kRopeTokens;
+  // Read first: loads complete in issue order, so a later frequency load would also wait
+  // for the rows below.  With kRopeThreads a multiple of r/2 a thread's table column is
+  // the same on every pass.
+  const bool one_col = kRopeThreads % half == 0;
+  const float freq0 = tab.inv_freq[threadIdx.x % half];
+
+  const int h_lo = q == nullptr ? kHq : 0;
+  const int h_hi = k == nullptr ? kHq : kHq + kHkv;
+  const int groups = half >> 3;                 // 8 pairs per item
+  const int per_tok = (h_hi - h_lo) * groups;
+  const int items = kRopeTokens * per_tok;
+
+  // The first item's rows are loaded before the table, so their latency overlaps it.
+  int t1 = 0, d1 = 0;
+  bf16_t* row1 = (int)threadIdx.x < items
+                     ? rope_item(q, k, tok0, ntok, threadIdx.x, h_lo, groups, per_tok, &t1, &d1)
+                     : nullptr;
+  uint4 xa1{}, xb1{};
+  if (row1 != nullptr) {
+    xa1 = *reinterpret_cast<const uint4*>(row1 + d1);
+    xb1 = *reinterpret_cast<const uint4*>(row1 + d1 + half);
+  }
 
   for (int e = threadIdx.x; e < kRopeTokens * half; e += kRopeThreads) {
     const int t = e / half, f = e - t * half;
@@ -35,31 +73,26 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(
       const int b = (int)(tok / S), s = (int)(tok - (long long)b * S);
       const int p = pos0[b] + s;
       float sv, cv;
-      sincos_angle(rope_angle(p, tab.inv_freq[f]), &sv, &cv);
+      sincos_angle(rope_angle(p, one_col ? freq0 : tab.inv_freq[f]), &sv, &cv);
       cs[t][f] = f32x2{cv, sv};
     }
   }
   __syncthreads();
 
-  const int groups = half >> 3;              // 8 pairs per item
-  const int per_tok = (kHq + kHkv) * groups;  // heads 0..15 of q, then 4 of k
-  for (int e = threadIdx.x; e < kRopeTokens * per_tok; e += kRopeThreads) {
-    const int t = e / per_tok;
-    const int rem = e - t * per_tok;
-    const int hh = rem / groups, gi = rem - hh * groups;
-    const long long tok = tok0 + t;
-    if (tok >= ntok) continue;
+  for (int e = threadIdx.x; e < items; e += kRopeThreads) {
+    int t, d0;
     bf16_t* row;
-    if (hh < kHq) {
-      if (q == nullptr) continue;
-      row = q + (tok * kHq + hh) * kD;
+    uint4 xa, xb;
+    if (e == (int)threadIdx.x) {
+      row = row1; t = t1; d0 = d1; xa = xa1; xb = xb1;
     } else {
-      if (k == nullptr) continue;
-      row = k + (tok * kHkv + (hh - kHq)) * kD;
+      row = rope_item(q, k, tok0, ntok, e, h_lo, groups, per_tok, &t, &d0);
+      if (row != nullptr) {
+        xa = *reinterpret_cast<const uint4*>(row + d0);
+        xb = *reinterpret_cast<const uint4*>(row + d0 + half);
+      }
     }
-    const int d0 = gi * 8;
-    uint4 xa = *reinterpret_cast<const uint4*>(row + d0);
-    uint4 xb = *reinterpret_cast<const uint4*>(row + d0 + half);
+    if (row == nullptr) continue;
     uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
     uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
     uint32_t ya[4], yb[4];
