@@ -498,22 +498,24 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
   }
 }
 
-// Grid (B * 16 query heads, 256 / 32 dim slices); 256 threads = 32 dims x 8 chunk groups.
-// Pass 1: the largest chunk max.  Pass 2: each chunk group folds every 8th chunk's partial
-// with weight 2^(m_c - M); the 8 groups are summed through LDS.
+// Grid (B * 16 query heads, 256 / 32 dim slices); 256 threads = 8 four-dim quads x 32
+// chunk groups, each thread loading 16 bytes of a chunk's partial output.  Pass 1: the
+// largest chunk max.  Pass 2: each chunk group folds every 32nd chunk's partial with weight
+// 2^(m_c - M); the 32 groups are summed through LDS.
 constexpr int kCombDims = 32;
-constexpr int kCombGroups = 8;
+constexpr int kCombQuads = kCombDims / 4;
+constexpr int kCombGroups = 256 / kCombQuads;
 
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int nchunks,
     const bf16_t* __restrict__ gate, bf16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float red_o[kCombGroups][kCombDims];
+  __shared__ f32x4 red_o[kCombGroups][kCombQuads];
   __shared__ float red_l[kCombGroups];
   __shared__ float red_m[4];
   const int b = blockIdx.x / kHq, h = blockIdx.x % kHq;
   const int kvh = h / kGroup, hl = h % kGroup;
-  const int dl = threadIdx.x & (kCombDims - 1), cg = threadIdx.x / kCombDims;
-  const int d = blockIdx.y * kCombDims + dl;
+  const int dq = threadIdx.x & (kCombQuads - 1), cg = threadIdx.x / kCombQuads;
+  const int d = blockIdx.y * kCombDims + 4 * dq;
   const long long base = (long long)(b * kHkv + kvh) * nchunks;
 
   float M = -INFINITY;
@@ -526,18 +528,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const float M_use = M == -INFINITY ? 0.f : M;
 
   // Eight chunks per batch, their loads issued before any of their arithmetic (indices
-  // past the last chunk read the last one and get weight 0), so that a thread has 24 loads
-  // in flight: the loop is bound by load latency, not bandwidth.
+  // past the last chunk read the last one and get weight 0): the loop is bound by load
+  // latency, so the chunks are spread over as many groups as the workgroup holds.
   constexpr int kBatch = 8;
-  float L = 0.f, acc = 0.f;
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = cg; c0 < nchunks; c0 += kBatch * kCombGroups) {
-    float mv[kBatch], lv[kBatch], ov[kBatch];
+    float mv[kBatch], lv[kBatch];
+    f32x4 ov[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const long long pc = (base + min(c0 + u * kCombGroups, nchunks - 1)) * kGroup + hl;
       mv[u] = ws_ml[pc * 2];
       lv[u] = ws_ml[pc * 2 + 1];
-      ov[u] = ws_o[pc * kD + d];
+      ov[u] = *reinterpret_cast<const f32x4*>(ws_o + pc * kD + d);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -546,21 +550,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
       acc += ov[u] * wgt;
     }
   }
-  red_o[cg][dl] = acc;
-  if (dl == 0) red_l[cg] = L;
+  red_o[cg][dq] = acc;
+  if (dq == 0) red_l[cg] = L;
   __syncthreads();
-  if (cg == 0) {
+  if (threadIdx.x < kCombDims) {
+    const int dl = threadIdx.x;
     float Lt = 0.f, at = 0.f;
 #pragma unroll
     for (int g2 = 0; g2 < kCombGroups; ++g2) {
       Lt += red_l[g2];
-      at += red_o[g2][dl];
+      at += red_o[g2][dl >> 2][dl & 3];
     }
     const long long row = (long long)b * kHq + h;
     const float g = bf16_to_f32(gate[row]);
     const float sg = 1.f / (1.f + expf(-g));
-    out[row * kD + d] = f32_to_bf16(Lt > 0.f ? at * (sg / Lt) : 0.f);
-    if (d == 0 && lse != nullptr) lse[row] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
+    const int dd = blockIdx.y * kCombDims + dl;
+    out[row * kD + dd] = f32_to_bf16(Lt > 0.f ? at * (sg / Lt) : 0.f);
+    if (dd == 0 && lse != nullptr) lse[row] = Lt > 0.f ? (M + log2f(Lt)) * kLn2 : -INFINITY;
   }
 }
 
