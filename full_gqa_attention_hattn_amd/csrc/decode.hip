@@ -581,11 +581,15 @@ constexpr int kRingWaves = 4;  // waves of the fused ring step
 // The cos/sin of p * omega_i are computed once and serve both the key and the query.
 // [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
 // tokens); [T3] "Sliding window 512" (RoPE theta 1e4 over all 256 dims).
+// kAppend: the step's append is fused in (the schedule driver); otherwise the token's key
+// and value are already in the ring (a plain sliding decode), and rope_q says whether q
+// still needs its rotation.
+template <bool kAppend>
 __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
     const bf16_t* __restrict__ v_new, bf16_t* __restrict__ k_ring, bf16_t* __restrict__ v_ring,
     const int* __restrict__ pos, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
-    float* __restrict__ lse, RopeTable tab, float sl2) {
+    float* __restrict__ lse, RopeTable tab, float sl2, int rope_q) {
   constexpr int kSlots = 512;
   constexpr int kHalf = 128;       // rot_dim / 2
   constexpr int kPerWave = kSlots / kRingWaves;
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
       qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
   }
 
-  if (tid < kHalf) {
+  if (tid < kHalf && (kAppend || rope_q)) {
     float sv, cv;
     sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
     cs[tid] = f32x2{cv, sv};
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
   __syncthreads();
 
   const long long ring_off = ((long long)b * kSlots * kHkv + kvh) * kD;
-  if (p >= 0) {
+  if (kAppend && p >= 0) {
     const long long row = ring_off + (long long)(p & (kSlots - 1)) * kHkv * kD;
     const long long src = ((long long)b * kHkv + kvh) * kD;
     if (tid < kHalf / 8) {
@@ -651,7 +655,7 @@ __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
   __syncthreads();
 
   // Q^T operand as in the split kernel (loaded first, above), rotated with the shared table.
-  if (qlane) {
+  if (qlane && rope_q) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       const bf16x8 xa = qf[dc], xb = qf[dc + 4];
@@ -1037,9 +1041,9 @@ hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* 
                        dim3(64 * kSplitWaves), 0, stream, q, k_new, v_new, k_ring, v_ring, pos,
                        gate, out, lse, tab, scale_log2e, ws_o, ws_ml, counters, 1);
   } else {
-    hipLaunchKernelGGL(ring_step_kernel, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves), 0,
-                       stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out, lse, tab,
-                       scale_log2e);
+    hipLaunchKernelGGL(ring_step_kernel<true>, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves),
+                       0, stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out, lse, tab,
+                       scale_log2e, 1);
   }
   return hipGetLastError();
 }
@@ -1048,7 +1052,14 @@ hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_
                               const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
                               bool rope_q, const RopeTable& tab, float scale_log2e,
                               void* workspace, hipStream_t stream) {
-  if (B > kRingSplitMaxB) return hipErrorInvalidValue;
+  if (B > kRingSplitMaxB) {
+    // The fused kernel without its append, one workgroup per (KV head, b); no workspace.
+    hipLaunchKernelGGL(ring_step_kernel<false>, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves),
+                       0, stream, q, nullptr, nullptr, const_cast<bf16_t*>(k_ring),
+                       const_cast<bf16_t*>(v_ring), pos, gate, out, lse, tab, scale_log2e,
+                       rope_q ? 1 : 0);
+    return hipGetLastError();
+  }
   const hipError_t e = clear_ring_counters(workspace, B, stream);
   if (e != hipSuccess) return e;
   const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
@@ -1063,6 +1074,6 @@ hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_
   return hipGetLastError();
 }
 
-bool ring_decode_applies(int B) { return B <= kRingSplitMaxB; }
+bool ring_decode_applies(int B) { return B >= 1; }
 
 }  // namespace hattn

@@ -71,9 +71,10 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
 // KV head), which must be zero before the first step (clear_ring_counters) and which every
 // step leaves at zero; larger batches use one workgroup each and no workspace.
 size_t ring_step_workspace_bytes(int B);
-// The same split attention for a plain sliding decode (the token's key and value already in
-// the ring; q rotated unless rope_q), for B with ring_decode_applies(B): clears the counters
-// and launches, in that order, on `stream`.
+// The same ring attention for a plain sliding decode (the token's key and value already in
+// the ring; q rotated unless rope_q), for every B >= 1 (ring_decode_applies): at B <= 2 it
+// clears the split kernel's counters and launches it, in that order, on `stream`; above,
+// it launches the fused kernel without its append and uses no workspace.
 bool ring_decode_applies(int B);
 hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_t* v_ring,
                               const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
