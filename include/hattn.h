@@ -177,10 +177,11 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
  *            order from position 0), and every valid slot is visible.
  * Same arithmetic as hattn_prefill.  The key range is split into chunks whose partial
  * (max, sum, output) triples are merged by log-sum-exp in a second kernel.  A sliding
- * layer at B <= 2 runs as one kernel instead: 8 workgroups per (sequence, KV head) each
- * take 64 ring slots, and the last of them to finish merges the 8 partials.  Its arrival
+ * layer runs as one kernel instead.  At B <= 2, 8 workgroups per (sequence, KV head) each
+ * take 64 ring slots, and the last of them to finish merges the 8 partials; its arrival
  * counters live in the workspace and the call clears them first, so calls that share a
- * workspace must be ordered (one stream); they race otherwise.
+ * workspace must be ordered (one stream); they race otherwise.  Above B = 2 one workgroup
+ * per (sequence, KV head) covers the ring and merges its waves' partials itself.
  * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes.
  * B <= 65535 (one grid row per sequence), else HATTN_ERR_SHAPE.
  * [T2] "The real bottleneck of a million-token context" (the ring keeps the last 512
