@@ -434,11 +434,6 @@ def attention_pairs_prefill(sq: int, pos0: int, kind) -> int:
     return int(short + (sq - n_short) * k.window)
 
 
-def sdpa_flops_per_pair() -> int:
-    """4 * head_dim flops per visible (query, key, head): QK^T and PV, 2 each per dim."""
-    return 4 * HEAD_DIM
-
-
 __all__ = [
     "N_Q_HEADS", "N_KV_HEADS", "HEAD_DIM", "SOFTMAX_SCALE", "WINDOW", "N_LAYERS",
     "LayerKind", "SLIDING", "FULL", "KINDS", "kind_of", "layer_schedule",
@@ -448,5 +443,4 @@ __all__ = [
     "kv_bytes_per_token_layer", "kv_cache_bytes", "attention_pairs_prefill",
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "kv_quantize", "kv_dequantize", "decode_kv8",
     "kv8_bytes_per_token_layer", "HIDDEN", "Q_DIM", "KV_DIM", "qkv_proj", "o_proj",
-    "sdpa_flops_per_pair",
 ]

@@ -74,3 +74,50 @@ def check_needle_row(gpu_out, gpu_lse, ref_out, ref_lse, name):
     err = (g - r).abs()
     assert bool((err <= 1e-2 + 2 ** -7 * r.abs()).all()), f"{name}: LSE err {float(err.max()):.3e}"
     say(f"{name}: max abs err {e1:.2e}, LSE err {float(err.max()):.2e}")
+
+
+def assert_rotated(gpu, ref, src, rot_dim, name):
+    """Keys or queries rotated on the GPU (bf16) against the oracle's rotation of the same
+    source (fp32): the rotated dims within one bf16 rounding and, for more than 98% of
+    them, equal to the round-to-nearest of the oracle; the pass-through dims equal to the
+    source bit for bit."""
+    g = gpu.detach().cpu()
+    r = ref.detach().cpu()
+    err = (g[..., :rot_dim].double() - r[..., :rot_dim].double()).abs()
+    bound = 2 ** -8 * r[..., :rot_dim].double().abs() + 1e-5
+    assert bool((err <= bound).all()), f"{name}: rotated dims off by {float((err - bound).max()):.3e}"
+    exact = float((g[..., :rot_dim] == r[..., :rot_dim].to(torch.bfloat16)).double().mean())
+    assert exact > 0.98, f"{name}: only {exact:.3f} of rotated dims round-to-nearest"
+    if rot_dim < g.shape[-1]:
+        assert torch.equal(g[..., rot_dim:], src.detach().cpu()[..., rot_dim:]), \
+            f"{name}: pass-through dims changed"
+
+
+def row_blocks(rows, block=64):
+    """Sorted distinct query rows in blocks of `block`, so the oracle's key range and its
+    score matrices stay those of one block."""
+    rows = sorted(set(int(r) for r in rows))
+    for i in range(0, len(rows), block):
+        yield torch.tensor(rows[i:i + block])
+
+
+class Coverage:
+    """Counts the (row, head) outputs an oracle comparison covered, for the report."""
+
+    def __init__(self, name, total_rows, unit="rows"):
+        self.name, self.total, self.rows, self.unit = name, int(total_rows), 0, unit
+        self.worst_abs = self.worst_rel = self.worst_lse = 0.0
+
+    def check(self, gpu_out, gpu_lse, ref_out, ref_lse):
+        e1 = assert_bf16_close(gpu_out, ref_out, self.name)
+        e2 = assert_rel_l2(gpu_out, ref_out, self.name)
+        e3 = assert_lse_close(gpu_lse, ref_lse, self.name)
+        self.rows += int(ref_out.shape[0])
+        self.worst_abs = max(self.worst_abs, e1)
+        self.worst_rel = max(self.worst_rel, e2)
+        self.worst_lse = max(self.worst_lse, e3)
+
+    def report(self):
+        say(f"{self.name}: checked {self.rows} of {self.total} {self.unit} "
+            f"({100.0 * self.rows / self.total:.2f}%), every head and dim; max abs err "
+            f"{self.worst_abs:.2e}, worst rel-L2 {self.worst_rel:.2e}, LSE err {self.worst_lse:.2e}")

@@ -298,3 +298,56 @@ def test_projection_validation(h):
         assert op(**{k: MIS}) == h.HATTN_ERR_ALIGN, k
     assert op(T=-1) == h.HATTN_ERR_SHAPE
     assert op(T=0, a=None) == h.HATTN_OK
+
+
+# --------------------------------------------------------------- binding marshalling --
+def test_binding_rejects_wrong_tensors_before_the_abi(h):
+    """The Python binding checks dtype, shape and device of every tensor before its pointer
+    crosses the C ABI (which cannot see sizes): a short output, an fp32 cache or a
+    host-resident position array is a ValueError, never an out-of-bounds device access.
+    Runs on host tensors, so every call below stops in the binding."""
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    cfg = h.preset("full")
+    B, S, cap = 2, 8, 64
+    q = torch.zeros(B, S, 16, 256, dtype=bf)
+    K = torch.zeros(B, cap, 4, 256, dtype=bf)
+    g = torch.zeros(B, S, 16, dtype=bf)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(B, S, 16, dtype=f32)
+    pos = torch.zeros(B, dtype=i32)
+
+    def raises(fn, *a, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    # well-formed arguments, but in host memory: the device check fires last
+    raises(h.prefill, cfg, q, K, K, pos, g, out, lse, match="GPU memory")
+    raises(h.prefill, cfg, q, K.float(), K, pos, g, out, lse, match="k_cache must be torch.bfloat16")
+    raises(h.prefill, cfg, q, K, K, pos, g, out[:, :S - 1].contiguous(), lse, match="out must have shape")
+    raises(h.prefill, cfg, q, K, K[:, :cap - 1].contiguous(), pos, g, out, lse, match="v_cache must have shape")
+    raises(h.prefill, cfg, q, K, K, pos[:1], g, out, lse, match="pos0 holds 1 elements")
+    raises(h.prefill, cfg, q, K, K, pos.long(), g, out, lse, match="pos0 must be torch.int32")
+    raises(h.prefill, cfg, q, K, K, pos, g, out, lse[..., :15].contiguous(), match="lse must have shape")
+    raises(h.decode, cfg, q, K, K, pos, g, out, lse, match="q must have shape")
+    qd, gd = q[:, :1].contiguous(), g[:, :1].contiguous()
+    raises(h.decode, cfg, qd, K, K, pos, gd, out[:, :1].contiguous(), lse[:, :1].contiguous(),
+           torch.zeros(16, dtype=f32), match="workspace must be torch.uint8")
+    raises(h.rope_qk, cfg, q, K[:, :S].contiguous(), pos, match="GPU memory")
+    raises(h.rope_qk, cfg, q, torch.zeros(B, S, 16, 256, dtype=bf), pos, match="k must have shape")
+    kn = torch.zeros(B, S, 4, 256, dtype=bf)
+    raises(h.kv_append, cfg, kn, kn, K, K, pos, torch.zeros(B, S - 1, dtype=i32),
+           match="slots_out must have shape")
+    raises(h.kv_append_fp8, cfg, kn, kn, K, K, lse, lse, pos, match="k_cache must be torch.uint8")
+    raises(h.prefill_ring, h.preset("sliding"), q, kn, kn, K, K, pos, g, out,
+           match="k_ring must have shape")
+    raises(h.o_proj, torch.zeros(3, 100, dtype=bf), torch.zeros(2560, 4096, dtype=bf),
+           torch.zeros(3, 2560, dtype=bf), match="whole 16 x 256 head rows")
+    raises(h.qkv_proj, torch.zeros(3, 2560, dtype=bf), torch.zeros(6144, 2560, dtype=bf),
+           torch.zeros(16, 2560, dtype=bf), torch.zeros(3, 16, 256, dtype=bf),
+           torch.zeros(2, 4, 256, dtype=bf), torch.zeros(3, 4, 256, dtype=bf),
+           torch.zeros(3, 16, dtype=bf), match="k holds 2048 elements")
+    layers = [dict(q=qd, k=kn[:, :1].contiguous(), v=kn[:, :1].contiguous(), gate=gd,
+                   k_cache=K, v_cache=K, out=out[:, :1].contiguous(), lse=None)]
+    raises(h.model_decode, layers, cap, pos, torch.zeros(16, dtype=torch.uint8),
+           match="layer 0 k_cache must have shape")      # layer 0 is sliding: a 512-slot ring

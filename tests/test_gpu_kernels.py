@@ -229,6 +229,7 @@ def _decode_case(h, kind, positions, cap, seed, fused):
     new = synth.layer_inputs(seed, B, 1, "cuda")
     cache = synth.cache_inputs(seed + 1, B, cap, cap, "cuda")
     K, V = cache["cache_k"], cache["cache_v"]
+    K0, V0 = K.clone(), V.clone()
     q = new["q"].clone()
     pos = synth.positions(positions, B, "cuda")
     if not fused:
@@ -238,6 +239,8 @@ def _decode_case(h, kind, positions, cap, seed, fused):
     ws = h.alloc_workspace(cfg, B, cap)
     h.decode(cfg, q, K, V, pos, new["gate"], out, lse, ws, rope_q_fused=fused)
     torch.cuda.synchronize()
+    # a decode only reads the caches (the ring kernels take them through const_cast)
+    assert torch.equal(K, K0) and torch.equal(V, V0), "decode wrote to the cache"
     for b, p in enumerate(positions):
         y, l = O.decode(_cpu(new["q"][b, 0]), _cpu(K[b]), _cpu(V[b]), _cpu(new["gate"][b, 0]),
                         p, kind)
@@ -251,7 +254,7 @@ def test_decode_full_cache(h, fused):
 
 
 @pytest.mark.parametrize("positions", [
-    [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9, (1 << 31) - 1],  # split + combine
+    [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9, (1 << 31) - 1],  # B > 2 ring kernel
     [131072],                                # B = 1 and 2: the ring split in one launch
     [300, (1 << 31) - 1],
 ])
@@ -320,3 +323,56 @@ def test_decode_equals_prefill_row(h):
             torch.cuda.synchronize()
             assert_bf16_close(od[0, 0], out[0, p].float(), f"{kind} p={p}", atol=4e-3, rtol=1e-2)
             assert float((ld[0, 0] - lse[0, p]).abs().max()) < 1e-3
+
+
+# ------------------------------------------------------------ split-count invariance --
+def test_decode_split_count_invariance(h):
+    """The same history decoded under different split plans agrees: the plan is a function
+    of (B, cap), so one sequence's 5000 keys are decoded in a cache of 5000 rows (157
+    chunks of 32 keys), in a cache of 65536 rows whose unused rows hold NaN (chunks of
+    128 keys, most past the history), and as sequence 7 of a batch of 32 copies (16 chunks
+    of 320 keys).  Also a sliding ring at B = 1 (the ring split over 8 workgroups) against
+    B = 3 (one workgroup per KV head), and a repeated call bit for bit."""
+    say("decode split-count invariance")
+    p, n = 4999, 5000
+    for kind in ("full", "sliding"):
+        cfg = h.preset(kind)
+        new = synth.layer_inputs(93, 1, 1, "cuda")
+        rows = n if kind == "full" else 512
+        hist = synth.cache_inputs(94, 1, rows, rows, "cuda")
+        pos = (p if kind == "full" else 131072 + 77)
+        results = []
+        plans = [(1, rows), (32, rows)] + ([(1, 65536)] if kind == "full" else [(3, rows)])
+        for B, cap in plans:
+            K = torch.full((B, cap, 4, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+            V = torch.full_like(K, float("nan"))
+            K[:, :rows] = hist["cache_k"]
+            V[:, :rows] = hist["cache_v"]
+            q = new["q"].expand(B, 1, 16, 256).contiguous()
+            g = new["gate"].expand(B, 1, 16).contiguous()
+            out = torch.empty_like(q)
+            lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
+            ws = h.alloc_workspace(cfg, B, cap)
+            ws.fill_(0xFF)
+            runs = []
+            for _ in range(2):
+                h.decode(cfg, q, K, V, synth.positions(pos, B, "cuda"), g, out, lse, ws,
+                         rope_q_fused=True)
+                torch.cuda.synchronize()
+                runs.append((out.clone(), lse.clone()))
+            assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1]), \
+                f"{kind} B={B} cap={cap}: repeated call differs"
+            sel = min(7, B - 1)
+            results.append((f"B={B} cap={cap}", out[sel, 0].float(), lse[sel, 0]))
+            if B > 1:   # every copy of the sequence gets the same answer
+                assert float((out.float() - out[:1].float()).abs().max()) < 1e-3
+        y, l = O.decode(_cpu(new["q"][0, 0]), _cpu(hist["cache_k"][0]), _cpu(hist["cache_v"][0]),
+                        _cpu(new["gate"][0, 0]), pos, kind)
+        for name, o, ls in results:
+            check_outputs(o, ls, y, l, f"invariance {kind} {name}")
+        base = results[0]
+        for name, o, ls in results[1:]:
+            d_out = float((o - base[1]).abs().max())
+            d_lse = float((ls - base[2]).abs().max())
+            say(f"  {kind} {name} vs {base[0]}: max |d out| {d_out:.2e}, max |d lse| {d_lse:.2e}")
+            assert d_out < 1e-3 and d_lse < 1e-4, (kind, name, d_out, d_lse)

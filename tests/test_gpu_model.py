@@ -6,7 +6,7 @@ import torch
 
 import oracle as O
 import synth
-from parity import assert_bf16_close, check_outputs, say
+from parity import assert_bf16_close, assert_rotated, check_outputs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +132,7 @@ def test_model_decode_graph_replay(h, positions):
         L["v_cache"].copy_(hist["cache_v"])
     pos = synth.positions(positions, B, "cuda")
     ws = torch.empty(h.model_decode_workspace_bytes(n_layers, B, cap), dtype=torch.uint8, device="cuda")
+    before = [(_cpu(L["k_cache"]).clone(), _cpu(L["v_cache"]).clone()) for L in layers]
     h.model_decode(layers, cap, pos, ws)
     torch.cuda.synchronize()
     ref = [(L["out"].clone(), L["lse"].clone()) for L in layers]
@@ -154,17 +155,22 @@ def test_model_decode_graph_replay(h, positions):
             assert torch.equal(L["out"], ref[l][0]), (rep, l)
             assert torch.equal(L["lse"], ref[l][1]), (rep, l)
         del junk
-    # and the eager result matches the oracle
+    # and the eager result matches the oracle's decode over the caches as they were before
+    # the step, with the oracle's own append of the oracle-rotated new key; every other
+    # cache row is unchanged by the replays
     p = positions
     for l, L in enumerate(layers):
         kind = L["kind"]
         for b in range(B):
             _, kn = O.rope_qk(None, _cpu(L["k"][b]), p[b], kind)
-            kc = _cpu(L["k_cache"][b]).float()
-            vc = _cpu(L["v_cache"][b]).float()
+            kc, vc = before[l][0][b].clone(), before[l][1][b].clone()
+            O.kv_append(kc, vc, kn.to(torch.bfloat16), _cpu(L["v"][b]), p[b], kind)
             slot = p[b] if kind == "full" else p[b] % 512
-            kc[slot] = kn[0]
-            vc[slot] = _cpu(L["v"][b, 0]).float()
+            other = torch.arange(kc.shape[0]) != slot
+            got_k, got_v = _cpu(L["k_cache"][b]), _cpu(L["v_cache"][b])
+            assert torch.equal(got_k[other], kc[other]) and torch.equal(got_v, vc), (l, b)
+            assert_rotated(got_k[slot], kn[0], L["k"][b, 0], O.KINDS[kind].rot_dim,
+                           f"graph layer {l} b={b} appended key")
             y, lse = O.decode(_cpu(L["q"][b, 0]), kc, vc, _cpu(L["gate"][b, 0]), p[b], kind)
             check_outputs(ref[l][0][b, 0], ref[l][1][b, 0], y, lse, f"graph layer {l} b={b}")
 
@@ -197,6 +203,7 @@ def test_model_decode_sliding_at_far_positions(h):
             assert torch.equal(got_k[torch.arange(512) != p % 512], K[torch.arange(512) != p % 512])
             assert_bf16_close(got_k[p % 512], kr[0], f"ring key layer {l} p={p}")
             assert torch.equal(_cpu(L["v_cache"][b]), V)
-            K[p % 512] = got_k[p % 512]          # attend over the ring the kernel wrote
+            assert_rotated(got_k[p % 512], kr[0], got_k[p % 512], 256, f"ring key layer {l} p={p}")
+            # the oracle attends over its own ring: the snapshot with its own rotated key
             y, lse = O.decode(_cpu(L["q"][b, 0]), K, V, _cpu(L["gate"][b, 0]), p, "sliding")
             check_outputs(L["out"][b, 0], L["lse"][b, 0], y, lse, f"model far layer {l} p={p}")
