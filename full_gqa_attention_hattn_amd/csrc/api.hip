@@ -68,15 +68,12 @@ int decode_max_keys(const hattn_layer_cfg* cfg, int32_t cap) {
   return cfg->kind == HATTN_SLIDING ? cfg->window : cap;
 }
 
-// Workspace a decode needs: the split partials, or for a sliding layer at small B the ring
-// split's partials and counters (whichever is larger, so one size serves both).
+// Workspace a decode needs: full layers, the split-KV partials; sliding layers, the ring
+// split's partials and counters at B <= 2 and nothing above (no partial leaves a
+// workgroup there).
 size_t decode_need(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
-  size_t need = hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));
-  if (cfg->kind == HATTN_SLIDING && hattn::ring_decode_applies(B)) {
-    const size_t r = hattn::ring_step_workspace_bytes(B);
-    need = need > r ? need : r;
-  }
-  return need;
+  if (cfg->kind == HATTN_SLIDING) return hattn::ring_step_workspace_bytes(B);
+  return hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));
 }
 
 }  // namespace
@@ -305,10 +302,10 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
   if (B > 65535 || (long long)B * cap >= (1LL << 40)) return HATTN_ERR_SHAPE;
   const hattn::DecodePlan plan = hattn::decode_plan(B, decode_max_keys(cfg, cap));
   const size_t need = decode_need(cfg, B, cap);
-  if (workspace == nullptr || workspace_bytes < need) return HATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return HATTN_ERR_ALIGN;
   const hattn::RopeTable tab = rope_table(cfg);
-  if (cfg->kind == HATTN_SLIDING && hattn::ring_decode_applies(B))
+  if (cfg->kind == HATTN_SLIDING)
     return hip_status(hattn::launch_ring_decode(
         static_cast<const hattn::bf16_t*>(q), static_cast<const hattn::bf16_t*>(k_cache),
         static_cast<const hattn::bf16_t*>(v_cache), pos, B,

@@ -70,13 +70,16 @@ __device__ __forceinline__ void load_step(StepRegs& r, const bf16_t* kb, const b
 }
 
 // One 32-key step on loaded operands: S^T = K . Q^T on MFMA, the online softmax and P.V on
-// the VALU, the probabilities going through this wave's slice `pl` of LDS.
+// the VALU, the probabilities going through this wave's slice `pl` of LDS.  The wave
+// attends NH query heads of the KV head (Q^T columns 0 .. NH - 1).
+template <int NH = kGroup>
 __device__ __forceinline__ void compute_step(const StepRegs& r, const bf16x8 (&qf)[8], int k0,
                                              int k_end, float sl2, float (*pl)[4], int lane,
-                                             float& m_run, float& l_run, float (&o)[kGroup][8]) {
+                                             float& m_run, float& l_run, float (&o)[NH][8]) {
+  static_assert(NH >= 1 && NH <= kGroup, "a wave attends at most one KV head's query heads");
   const int n16 = lane & 15, g = lane >> 4;
   const int half = lane >> 5;
-  const bool qlane = n16 < kGroup;
+  const bool qlane = n16 < NH;
   f32x4 s[2] = {f32x4{}, f32x4{}};
 #pragma unroll
   for (int dc = 0; dc < 8; ++dc) {
@@ -104,17 +107,12 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const bf16x8 (&q
     const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
     l_run *= alpha;
     m_run = m_new;
-    // Per-head factors live in lanes 0..3 (column = head, k-group 0).
-    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
-    const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
-    const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+    // Per-head factors live in lanes 0 .. NH - 1 (column = head, k-group 0).
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[0][e] *= a0;
-      o[1][e] *= a1;
-      o[2][e] *= a2;
-      o[3][e] *= a3;
+    for (int hl = 0; hl < NH; ++hl) {
+      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hl));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hl][e] *= a;
     }
   }
   const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -142,9 +140,9 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const bf16x8 (&q
   for (int kp = 0; kp < 16; kp += 2) {
     const f32x4 pa = *reinterpret_cast<const f32x4*>(&pl[2 * kp + half][0]);
     const f32x4 pb = *reinterpret_cast<const f32x4*>(&pl[2 * kp + 2 + half][0]);
-    bf16x2 pp[kGroup];
+    bf16x2 pp[NH];
 #pragma unroll
-    for (int hl = 0; hl < kGroup; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
+    for (int hl = 0; hl < NH; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
     const uint32_t* va = reinterpret_cast<const uint32_t*>(&r.vv[kp]);
     const uint32_t* vb2 = reinterpret_cast<const uint32_t*>(&r.vv[kp + 1]);
 #pragma unroll
@@ -152,7 +150,7 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const bf16x8 (&q
       const bf16x2 d0 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x05040100u));
       const bf16x2 d1 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(vb2[w], va[w], 0x07060302u));
 #pragma unroll
-      for (int hl = 0; hl < kGroup; ++hl) {
+      for (int hl = 0; hl < NH; ++hl) {
         o[hl][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(d0, pp[hl], o[hl][2 * w], false);
         o[hl][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(d1, pp[hl], o[hl][2 * w + 1], false);
       }
@@ -162,15 +160,17 @@ __device__ __forceinline__ void compute_step(const StepRegs& r, const bf16x8 (&q
 }
 
 // One wave's pass over keys [k_begin, k_end) of its KV head, one 32-key step at a time.
-// Leaves this lane's share of the partial (reference max, sum, o[head][8 dims]).
+// Leaves this lane's share of the partial (reference max, sum, o[head][8 dims]) of the NH
+// query heads it attends.
+template <int NH = kGroup>
 __device__ __forceinline__ void attend_keys(const bf16x8 (&qf)[8], const bf16_t* kb,
                                             const bf16_t* vb, int k_begin, int k_end, float sl2,
                                             float (*pl)[4], int lane, float& m_run, float& l_run,
-                                            float (&o)[kGroup][8]) {
+                                            float (&o)[NH][8]) {
   for (int k0 = k_begin; k0 < k_end; k0 += kStep) {
     StepRegs r;
     load_step(r, kb, vb, k0, k_end, lane);
-    compute_step(r, qf, k0, k_end, sl2, pl, lane, m_run, l_run, o);
+    compute_step<NH>(r, qf, k0, k_end, sl2, pl, lane, m_run, l_run, o);
   }
 }
 
@@ -727,6 +727,140 @@ __global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
   if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// Sliding decode above two sequences (the token's key and value already in the ring):
+// the query heads of each (sequence, KV head) are split over kGroup / NH workgroups, each
+// attending NH heads over the whole ring with kW waves of 512 / kW slots.  No partial
+// crosses workgroups, so there is no merge between them; the ring rows are read once per
+// workgroup, and the workgroups of one (sequence, KV head) run on one XCD (workgroup i
+// runs on XCD i mod 8), where the second read of those rows hits that XCD's L2.  At
+// B = 32 that fills the chip with 256 workgroups, where one workgroup per (sequence, KV
+// head) left half the CUs idle and ran each wave's four steps one after another.
+// [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
+// tokens); [T3] "Sliding window 512"; [T1] "GQA, fused projection and output gating".
+template <int NH, int kW>
+__global__ __launch_bounds__(64 * kW) void ring_heads_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_ring,
+    const bf16_t* __restrict__ v_ring, const int* __restrict__ pos, int B,
+    const bf16_t* __restrict__ gate, bf16_t* __restrict__ out, float* __restrict__ lse,
+    RopeTable tab, float sl2, int rope_q) {
+  constexpr int kSlots = 512;
+  constexpr int kHalf = 128;                 // rot_dim / 2
+  constexpr int kSplit = kGroup / NH;        // workgroups per (sequence, KV head)
+  constexpr int kPerWave = kSlots / kW;      // ring slots per wave
+  static_assert(kGroup % NH == 0 && kPerWave % kStep == 0, "ring split shape");
+  static_assert(64 * kW >= kHalf && 64 * kW >= 64 * NH, "table and merge thread counts");
+  __shared__ f32x2 cs[kHalf];
+  __shared__ __attribute__((aligned(16))) float p_lds[kW][kStep][4];
+  __shared__ __attribute__((aligned(16))) float part_o[kW][NH][kD];
+  __shared__ float part_ml[kW][NH][2];
+
+  // Workgroup id -> (XCD, j): the kSplit workgroups of (sequence, KV head) `grp` are
+  // ids 8 (kSplit g' + part) + xcd with grp = 8 g' + xcd, all on XCD xcd.
+  const int id = (int)blockIdx.x, xcd = id & 7, j = id >> 3;
+  const int part = j % kSplit;
+  const int grp = (j / kSplit) * 8 + xcd;
+  if (grp >= B * kHkv) return;
+  const int b = grp / kHkv, kvh = grp % kHkv;
+  const int h0 = kvh * kGroup + part * NH;   // first query head of this workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int half = lane >> 5, dg = lane & 31;
+  const int p = pos[b];
+
+  const bool qlane = n16 < NH;
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = q + ((long long)b * kHq + h0 + (qlane ? n16 : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+  }
+  if (rope_q) {
+    if (tid < kHalf) {
+      float sv, cv;
+      sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
+      cs[tid] = f32x2{cv, sv};
+    }
+    __syncthreads();
+    if (qlane) {
+#pragma unroll
+      for (int dc = 0; dc < 4; ++dc) {
+        const bf16x8 xa = qf[dc], xb = qf[dc + 4];
+        f32x4 ya0, ya1, yb0, yb1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x2 c = cs[32 * dc + 8 * g + e];
+          float ya, yb;
+          rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
+          if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
+        }
+        const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
+        const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
+        qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        qf[dc + 4] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      }
+    }
+  }
+
+  const long long ring_off = ((long long)b * kSlots * kHkv + kvh) * kD;
+  const int kv_len = p >= 0 ? min(p, kSlots - 1) + 1 : 0;  // no p + 1: p may be 2^31 - 1
+  const int k_begin = kPerWave * w;
+  const int k_end = min(kv_len, k_begin + kPerWave);
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[NH][8];
+#pragma unroll
+  for (int hl = 0; hl < NH; ++hl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
+  attend_keys<NH>(qf, k_ring + ring_off, v_ring + ring_off, k_begin, k_end, sl2, p_lds[w], lane,
+                  m_run, l_run, o);
+#pragma unroll
+  for (int hl = 0; hl < NH; ++hl)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hl][e] += __shfl_xor(o[hl][e], 32);
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (half == 0) {
+#pragma unroll
+    for (int hl = 0; hl < NH; ++hl) {
+      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg]) = f32x4{o[hl][0], o[hl][1], o[hl][2], o[hl][3]};
+      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg + 4]) = f32x4{o[hl][4], o[hl][5], o[hl][6], o[hl][7]};
+    }
+  }
+  if (lane < NH) {
+    part_ml[w][lane][0] = m_run;
+    part_ml[w][lane][1] = l_run;
+  }
+  __syncthreads();
+
+  // Merge the kW wave partials: thread (head hl, dims 4i .. 4i + 3).
+  if (tid >= 64 * NH) return;
+  const int hl = tid >> 6, d = 4 * (tid & 63);
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kW; ++v) M = fmaxf(M, part_ml[v][hl][0]);
+  const float M_use = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  f32x4 acc = f32x4{};
+#pragma unroll
+  for (int v = 0; v < kW; ++v) {
+    const float wgt = fast_exp2(part_ml[v][hl][0] - M_use);
+    L += part_ml[v][hl][1] * wgt;
+    acc += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d]) * wgt;
+  }
+  const long long row = (long long)b * kHq + h0 + hl;
+  const float gl = bf16_to_f32(gate[row]);
+  const float sg = 1.f / (1.f + expf(-gl));
+  const float f = L > 0.f ? sg / L : 0.f;
+  *reinterpret_cast<uint2*>(out + row * kD + d) =
+      uint2{pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f)};
+  if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+constexpr int kHeadsNH = 2;      // query heads per head-split ring workgroup
+constexpr int kHeadsWaves = 8;   // its waves (64 ring slots each)
+
 constexpr int kRingSlots = 512;                     // a sliding layer's ring
 constexpr int kRingSplits = 8;                      // workgroups per (KV head, sequence)
 constexpr int kSplitWaves = 2;                      // waves per split workgroup
@@ -993,15 +1127,11 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o + parts * kD;
   const dim3 grid((unsigned)plan.nchunks, (unsigned)B);
-  if (window > 0) {
-    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
-                       cap, pos, window, plan.chunk, plan.nchunks, ws_o, ws_ml, rope_q ? 1 : 0, tab,
-                       scale_log2e);
-  } else {
-    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
-                       cap, pos, window, plan.chunk, plan.nchunks, ws_o, ws_ml, rope_q ? 1 : 0, tab,
-                       scale_log2e);
-  }
+  // Full layers only: a sliding layer decodes through the ring kernels (launch_ring_decode).
+  if (window > 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(256), 0, stream, q, k_cache, v_cache,
+                     cap, pos, window, plan.chunk, plan.nchunks, ws_o, ws_ml, rope_q ? 1 : 0, tab,
+                     scale_log2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * kHq), kD / kCombDims), dim3(256), 0,
@@ -1053,11 +1183,12 @@ hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_
                               bool rope_q, const RopeTable& tab, float scale_log2e,
                               void* workspace, hipStream_t stream) {
   if (B > kRingSplitMaxB) {
-    // The fused kernel without its append, one workgroup per (KV head, b); no workspace.
-    hipLaunchKernelGGL(ring_step_kernel<false>, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves),
-                       0, stream, q, nullptr, nullptr, const_cast<bf16_t*>(k_ring),
-                       const_cast<bf16_t*>(v_ring), pos, gate, out, lse, tab, scale_log2e,
-                       rope_q ? 1 : 0);
+    // Query heads split over kGroup / kHeadsNH workgroups per (KV head, b); no workspace.
+    constexpr int kSplit = kGroup / kHeadsNH;
+    const unsigned grid = 8u * kSplit * (unsigned)((B * kHkv + 7) / 8);
+    hipLaunchKernelGGL((ring_heads_kernel<kHeadsNH, kHeadsWaves>), dim3(grid),
+                       dim3(64 * kHeadsWaves), 0, stream, q, k_ring, v_ring, pos, B, gate, out,
+                       lse, tab, scale_log2e, rope_q ? 1 : 0);
     return hipGetLastError();
   }
   const hipError_t e = clear_ring_counters(workspace, B, stream);
@@ -1074,6 +1205,5 @@ hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_
   return hipGetLastError();
 }
 
-bool ring_decode_applies(int B) { return B >= 1; }
 
 }  // namespace hattn

@@ -163,9 +163,10 @@ hattn_status hattn_prefill_ring(const hattn_layer_cfg* cfg, const void* q, const
                                 const int32_t* pos0, int32_t B, int32_t Sq, const void* gate,
                                 void* out, float* lse, uint32_t flags, void* stream);
 
-/* Bytes of device workspace hattn_decode needs for B sequences and this cache capacity
- * (its split-KV partial results; for a sliding layer at B <= 2 also its arrival
- * counters).  0 for an invalid configuration. */
+/* Bytes of device workspace hattn_decode needs for B sequences and this cache capacity:
+ * a full layer's split-KV partial results; a sliding layer's ring-split partials and
+ * arrival counters at B <= 2, and 0 above (no workspace).  0 also for an invalid
+ * configuration. */
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap);
 
 /* Single-token decode.  q [B,1,16,256] (rotated unless flags & HATTN_ROPE_Q_FUSED),
@@ -180,9 +181,11 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
  * layer runs as one kernel instead.  At B <= 2, 8 workgroups per (sequence, KV head) each
  * take 64 ring slots, and the last of them to finish merges the 8 partials; its arrival
  * counters live in the workspace and the call clears them first, so calls that share a
- * workspace must be ordered (one stream); they race otherwise.  Above B = 2 one workgroup
- * per (sequence, KV head) covers the ring and merges its waves' partials itself.
- * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes.
+ * workspace must be ordered (one stream); they race otherwise.  Above B = 2 the 4 query
+ * heads of each (sequence, KV head) are split over 2 workgroups, each covering the whole
+ * ring for its 2 heads and merging its waves' partials itself; no workspace is used.
+ * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes (16-byte
+ * aligned); may be NULL when that size is 0.
  * B <= 65535 (one grid row per sequence), else HATTN_ERR_SHAPE.
  * [T2] "The real bottleneck of a million-token context" (the ring keeps the last 512
  * tokens); [T1] "GQA, fused projection and output gating". */

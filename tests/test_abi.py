@@ -166,7 +166,10 @@ def test_decode_validation_and_workspace(h):
     f, s = _cfg(h, "full"), _cfg(h, "sliding")
     need = lib.hattn_decode_workspace_bytes(f, 32, 131136)
     assert need > 0 and need % 16 == 0
-    assert lib.hattn_decode_workspace_bytes(s, 32, 512) > 0
+    # sliding layers: the ring split's partials and counters at B <= 2, nothing above
+    assert lib.hattn_decode_workspace_bytes(s, 2, 512) > 0
+    assert lib.hattn_decode_workspace_bytes(s, 3, 512) == 0
+    assert lib.hattn_decode_workspace_bytes(s, 32, 512) == 0
     assert lib.hattn_decode_workspace_bytes(s, 32, 513) == 0
     assert lib.hattn_decode_workspace_bytes(f, -1, 8) == 0
 

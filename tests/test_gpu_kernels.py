@@ -236,7 +236,8 @@ def _decode_case(h, kind, positions, cap, seed, fused):
         h.rope_qk(cfg, q, None, pos)
     out = torch.empty_like(q)
     lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
-    ws = h.alloc_workspace(cfg, B, cap)
+    # sliding layers above two sequences need no workspace: pass none
+    ws = h.alloc_workspace(cfg, B, cap) if kind == "full" or B <= 2 else None
     h.decode(cfg, q, K, V, pos, new["gate"], out, lse, ws, rope_q_fused=fused)
     torch.cuda.synchronize()
     # a decode only reads the caches (the ring kernels take them through const_cast)
