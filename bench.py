@@ -463,6 +463,10 @@ def make_workload(idx: int, device="cuda"):
 
 
 # ---------------------------------------------------------------------- cpu baseline --
+def _blocks(rows, n=64):
+    return [rows[i:i + n] for i in range(0, len(rows), n)]
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload, timed on the
     host's cores.  Reported in the metric's unit (TFLOP/s of attention work; GB/s of KV
@@ -471,26 +475,33 @@ def cpu_baseline(wl, budget_s: float):
     torch.set_num_threads(os.cpu_count() or 1)
     cores = torch.get_num_threads()
     if isinstance(wl, Full1MWorkload):
-        rows = [wl.C - 1 - i for i in range(4)]
+        # the declared sample: the chunk's last 128 rows and 128 seeded random rows, the
+        # oracle run on 64-row blocks (its own row blocking), until the budget is spent
         kc = wl.K[0, :wl.L0].cpu()
         vc = wl.V[0, :wl.L0].cpu()
-        k_chunk = wl.k_src[0].cpu()
-        _, kr = O.rope_qk(None, k_chunk, wl.L0, "full")
+        _, kr = O.rope_qk(None, wl.k_src[0].cpu(), wl.L0, "full")
         kc = torch.cat([kc.to(torch.float32), kr])
         vc = torch.cat([vc.to(torch.float32), wl.v[0].cpu().to(torch.float32)])
         q, g = wl.q[0].cpu(), wl.gate[0].cpu()
+        gen = torch.Generator().manual_seed(1239)
+        rand = sorted(torch.randperm(wl.C - 128, generator=gen)[:128].tolist())
+        blocks = _blocks(list(range(wl.C - 128, wl.C))) + _blocks(rand)
         t0 = time.perf_counter()
         done = []
-        for r in rows:
-            O.prefill(q, kc, vc, g, wl.L0, "full", rows=torch.tensor([r]))
-            done.append(r)
+        for blk in blocks:
+            O.prefill(q, kc, vc, g, wl.L0, "full", rows=torch.tensor(blk))
+            done += blk
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
         flop = sum(HQ * FLOP_PER_PAIR * (wl.L0 + r + 1) for r in done)
-        return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-                "sample": f"prefill rows {done} of the 4096-query chunk over the full "
-                          f"{wl.L0 + wl.C}-token cache, all 16 heads ({dt:.1f} s)"}
+        rate = flop / dt
+        return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"declared sample of the 4096-query chunk (last 128 rows, then 128 "
+                          f"seeded random rows) over the full {wl.L0 + wl.C}-token cache, all "
+                          f"16 heads, oracle on 64-row blocks: {len(done)} rows timed in "
+                          f"{dt:.1f} s; the whole chunk extrapolated by visible-pair count "
+                          f"would take {wl.prefill_flop / rate:.0f} s"}
     if isinstance(wl, ProjWorkload):
         t0 = time.perf_counter()
         rows, flop = 0, 0
@@ -575,24 +586,37 @@ def cpu_baseline(wl, budget_s: float):
                 "sample": f"{len(done)} prefill rows of the 4096-query chunk against the "
                           f"ring, all 16 heads ({dt:.1f} s)"}
     if isinstance(wl, PrefillWorkload):
+        # sequence 0; full layer: the declared sample (last 1024 rows, 2048 seeded random
+        # rows, first 1024 rows); sliding layer: every row in order.  64-row blocks until
+        # the budget is spent, extrapolated by visible-pair count.
         b = 0
         S = wl.S
-        rows = list(range(S - 1, S - 65, -1))
+        if wl.kind == "full":
+            gen = torch.Generator().manual_seed(1237)
+            rand = sorted((torch.randperm(S - 2048, generator=gen)[:2048] + 1024).tolist())
+            blocks = (_blocks(list(range(S - 1024, S))) + _blocks(rand)
+                      + _blocks(list(range(1024))))
+            what = "declared sample (last 1024, 2048 seeded random, first 1024 rows)"
+        else:
+            blocks = _blocks(list(range(S)))
+            what = "every row in order"
         q, g = wl.q[b].cpu(), wl.gate[b].cpu()
         k_cpu, v = wl.k_src[b].cpu(), wl.v[b].cpu()
         _, kr = O.rope_qk(None, k_cpu, 0, wl.kind)
         t0 = time.perf_counter()
         done = []
-        for r in rows:
-            O.prefill(q, kr, v, g, 0, wl.kind, rows=torch.tensor([r]))
-            done.append(r)
+        for blk in blocks:
+            O.prefill(q, kr, v, g, 0, wl.kind, rows=torch.tensor(blk))
+            done += blk
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
         pairs = sum((r + 1) if wl.kind == "full" else min(r + 1, WINDOW) for r in done)
-        return {"value": HQ * FLOP_PER_PAIR * pairs / dt / 1e12, "unit": "TFLOP/s",
-                "cores": cores, "kind": "oracle",
-                "sample": f"{len(done)} prefill rows of sequence 0 ({dt:.1f} s)"}
+        rate = HQ * FLOP_PER_PAIR * pairs / dt
+        return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"sequence 0, {what}, oracle on 64-row blocks: {len(done)} rows "
+                          f"timed in {dt:.1f} s; the whole workload extrapolated by "
+                          f"visible-pair count would take {wl.prefill_flop / rate:.0f} s"}
     # mixed decode: full-layer decode of a few sequences
     L = wl.layers[0]
     t0 = time.perf_counter()
@@ -689,42 +713,25 @@ def model_fields(rec, wl, ms, stage_ms):
 
 
 # ------------------------------------------------------------------------------ main --
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=list(range(2, 12)))
-    ap.add_argument("--cpu-budget", type=float, default=20.0,
-                    help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="run one plain device copy of this many MiB before the workload "
-                         "(for calibrating HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(2)
-
-    copy_calibration(args.copy_calibration_mib)
-    wl = make_workload(args.workload)
+def measure(idx: int, steps: int, warmup: int, cpu_budget: float, calib_mib: int = 0):
+    """Build workload idx, run `warmup` untimed steps, then time exactly `steps` steps
+    between two device synchronisations; returns the workload's JSON record."""
+    copy_calibration(calib_mib)
+    wl = make_workload(idx)
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
     wl.stages.clear()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         wl.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms = (t1 - t0) * 1e3 / steps
 
     st = wl.stages
-    rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+    rec = {"metric": METRIC, "n_gpus": 1, "steps": steps, "warmup": warmup,
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16; no weights needed)"}
     stage_ms = {k: st.mean_ms(k) for k in st.t if st.t[k]}
@@ -752,7 +759,7 @@ def main():
         rec["prefill_frac_mfma_peak"] = achieved / PEAK_BF16_TFLOPS
         tr_name = {5: "prefill_full_1m_chunk4096", 3: "prefill_full_b1_s131072",
                    2: "prefill_sliding_b4_s32768",
-                   6: "prefill_sliding_ring_1m_chunk4096"}[args.workload]
+                   6: "prefill_sliding_ring_1m_chunk4096"}[idx]
         rec["roofline"] = {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,
@@ -766,7 +773,7 @@ def main():
         rec["decode_frac_hbm_peak"] = gbps / PEAK_HBM_GBPS
         rec["keys_per_s"] = wl.B * (wl.P + 1) / (dec_ms * 1e-3)
         rec["kv_bytes_per_token_layer"] = wl.kv8_bytes_per_token
-        name = {9: "decode_fp8_full_1m", 10: "decode_fp8_full_b32_p131072"}[args.workload]
+        name = {9: "decode_fp8_full_1m", 10: "decode_fp8_full_b32_p131072"}[idx]
         rec["roofline"] = {"bound": "hbm", "kernel": "decode_split_fp8_kernel+combine",
                            "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                            "frac": gbps / PEAK_HBM_GBPS,
@@ -789,10 +796,60 @@ def main():
                                "traffic": measured_traffic("decode.hip", "decode_full_b32_p131072")}
     W = wl.W
     rec["config"] = {"workload": W.name, "desc": W.desc, **W.params}
-    if args.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    rec["cpu_baseline"] = cpu_baseline(wl, cpu_budget) if cpu_budget > 0 else None
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+# The metric names the 128K and 1M contexts: besides the headline 1M workload, the default
+# run times the 32K sliding prefill, the 128K full prefill and the B=32 decode at 128K.
+DEFAULT_EXTRA = (2, 3, 4)
+_CONFIG_KEYS = ("ms_per_step", "value", "unit", "stage_ms", "roofline", "decode_GBps",
+                "decode_frac_hbm_peak", "prefill_TFLOPs_kernel", "prefill_frac_mfma_peak",
+                "config", "cpu_baseline")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5, choices=list(range(2, 12)))
+    ap.add_argument("--extra", type=str, default=None,
+                    help="comma-separated workloads also timed and reported under 'configs' "
+                         "(default 2,3,4 with workload 5, none otherwise; 'none' for none)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--extra-cpu-budget", type=float, default=4.0,
+                    help="seconds of oracle work for each extra workload's cpu_baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the workload "
+                         "(for calibrating HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU (no collectives or "
+                                   "sharding are built); run with --gpus 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    if args.extra is None:
+        extra = DEFAULT_EXTRA if args.workload == 5 else ()
+    elif args.extra.strip().lower() in ("", "none"):
+        extra = ()
     else:
-        rec["cpu_baseline"] = None
+        extra = tuple(int(x) for x in args.extra.split(","))
+
+    rec = measure(args.workload, args.steps, args.warmup, args.cpu_budget,
+                  args.copy_calibration_mib)
+    if extra:
+        rec["configs"] = []
+        for idx in extra:
+            r = measure(idx, args.steps, args.warmup, args.extra_cpu_budget)
+            rec["configs"].append({k: r[k] for k in _CONFIG_KEYS if k in r})
     print(json.dumps(rec), flush=True)
 
 
