@@ -390,7 +390,7 @@ class Kv8DecodeWorkload:
         self.pos = synth.positions(P, B, device)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(B, 1, HQ, dtype=torch.float32, device=device)
-        self.ws = hattn.alloc_workspace(self.cfg, B, self.cap, device)
+        self.ws = hattn.alloc_workspace_fp8(self.cfg, B, self.cap, device)
         self.stages = Stages(["append", "decode"])
         self.prefill_flop = 0
         self.kv8_bytes_per_token = 2 * HKV * D + 2 * HKV * 4

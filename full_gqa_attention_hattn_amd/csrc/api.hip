@@ -278,6 +278,13 @@ hattn_status hattn_decode_fp8(const hattn_layer_cfg* cfg, const void* q, const v
       scale_log2e(cfg), plan, workspace, as_stream(stream)));
 }
 
+size_t hattn_decode_fp8_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
+  if (check_cfg(cfg) != HATTN_OK || B < 0 || cap < 1) return 0;
+  if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return 0;
+  if (B == 0) return 0;
+  return hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));
+}
+
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
   if (check_cfg(cfg) != HATTN_OK || B < 0 || cap < 1) return 0;
   if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return 0;

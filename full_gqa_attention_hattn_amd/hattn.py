@@ -30,6 +30,7 @@ HATTN_KV8_ROPE_K = 1
 # Every symbol include/hattn.h declares.
 EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_kv_append_rope",
            "hattn_prefill", "hattn_prefill_ring", "hattn_kv_append_fp8", "hattn_decode_fp8",
+           "hattn_decode_fp8_workspace_bytes",
            "hattn_qkv_proj", "hattn_o_proj",
            "hattn_decode_workspace_bytes", "hattn_decode", "hattn_model_layer_kind",
            "hattn_model_kv_bytes", "hattn_model_decode_workspace_bytes", "hattn_model_decode",
@@ -83,6 +84,8 @@ def _load():
     lib.hattn_decode_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
                                      ctypes.c_size_t, u32, vp]
     lib.hattn_decode_fp8.restype = i32
+    lib.hattn_decode_fp8_workspace_bytes.argtypes = [cfgp, i32, i32]
+    lib.hattn_decode_fp8_workspace_bytes.restype = ctypes.c_size_t
     iop = ctypes.POINTER(LayerIO)
     sz = ctypes.c_size_t
     lib.hattn_model_layer_kind.argtypes = [i32]
@@ -396,6 +399,12 @@ def kv_append_fp8(cfg: LayerCfg, k_new, v_new, k_cache, v_cache, k_scale, v_scal
                                     _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), cap, _ptr(pos0),
                                     B, n, _ptr(slots_out), HATTN_KV8_ROPE_K if rope_k else 0,
                                     _stream(stream)), "hattn_kv_append_fp8")
+
+
+def alloc_workspace_fp8(cfg: LayerCfg, B: int, cap: int, device="cuda"):
+    """Workspace of decode_fp8 (its split-KV partials, for both layer kinds)."""
+    n = int(_lib.hattn_decode_fp8_workspace_bytes(ctypes.byref(cfg), int(B), int(cap)))
+    return torch.empty(max(16, n), dtype=torch.uint8, device=device)
 
 
 def decode_fp8(cfg: LayerCfg, q, k_cache, v_cache, k_scale, v_scale, pos, gate, out, lse=None,

@@ -220,8 +220,10 @@ hattn_status hattn_kv_append_fp8(const hattn_layer_cfg* cfg, const void* k_new,
                                  int32_t n, int32_t* slots_out, uint32_t flags, void* stream);
 
 /* hattn_decode over an 8-bit cache: the attention of the dequantized keys and values (the
- * key scale multiplies its score, the value scale its probability).  Arguments, workspace
- * (hattn_decode_workspace_bytes), flags and errors as hattn_decode. */
+ * key scale multiplies its score, the value scale its probability).  Arguments, flags and
+ * errors as hattn_decode; the workspace (16-byte aligned) holds the split-KV partials for
+ * both layer kinds: at least hattn_decode_fp8_workspace_bytes(cfg, B, cap) bytes. */
+size_t hattn_decode_fp8_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap);
 hattn_status hattn_decode_fp8(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
                               const void* v_cache, const float* k_scale, const float* v_scale,
                               int32_t cap, const int32_t* pos, int32_t B, const void* gate,

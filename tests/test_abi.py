@@ -190,6 +190,19 @@ def test_decode_validation_and_workspace(h):
     assert call(B=0) == h.HATTN_OK
 
 
+def test_decode_fp8_workspace_holds_the_split_for_both_kinds(h):
+    """The 8-bit decode splits the keys for both layer kinds, so its workspace is the split
+    partials even where the bf16 sliding decode needs none (B > 2)."""
+    lib = h.lib()
+    f, s = _cfg(h, "full"), _cfg(h, "sliding")
+    for B in (1, 2, 3, 32):
+        n = lib.hattn_decode_fp8_workspace_bytes(s, B, 512)
+        assert n >= B * 4 * 4 * 258 * 4 and n % (B * 4 * 4 * 258 * 4) == 0, B
+    assert lib.hattn_decode_fp8_workspace_bytes(s, 3, 513) == 0
+    assert lib.hattn_decode_fp8_workspace_bytes(f, 32, 131136) == \
+        lib.hattn_decode_workspace_bytes(f, 32, 131136)
+
+
 def test_decode_workspace_scales_with_plan(h):
     lib = h.lib()
     f = _cfg(h, "full")

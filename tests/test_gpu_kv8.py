@@ -120,7 +120,7 @@ def test_decode_fp8_matches_oracle(h, kind, fused):
         h.rope_qk(cfg, q, None, pos)
     out = torch.empty_like(q)
     lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
-    ws = h.alloc_workspace(cfg, B, cap)
+    ws = h.alloc_workspace_fp8(cfg, B, cap)
     h.decode_fp8(cfg, q, Kd, Vd, Ksd, Vsd, pos, new["gate"], out, lse, ws, rope_q_fused=fused)
     torch.cuda.synchronize()
     for b, p in enumerate(positions):
@@ -145,7 +145,7 @@ def test_decode_fp8_follows_append_fp8(h):
     g = inp["gate"][:, p:p + 1].contiguous()
     out = torch.empty_like(q)
     lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
-    ws = h.alloc_workspace(cfg, B, cap)
+    ws = h.alloc_workspace_fp8(cfg, B, cap)
     h.decode_fp8(cfg, q, Kc, Vc, Ks, Vs, synth.positions(p, B, "cuda"), g, out, lse, ws,
                  rope_q_fused=True)
     torch.cuda.synchronize()
