@@ -3,6 +3,7 @@
 // guards for the device-resident position arrays.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/hattn.h"
 #include "hattn_device.h"
@@ -292,25 +293,39 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
   return decode_need(cfg, B, cap);
 }
 
-hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+}  // extern "C"
+
+namespace {
+
+// Checks of a decode call's arguments other than its workspace; *done is set when the
+// call is empty (B == 0) and nothing is to be launched.
+hattn_status check_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
                           const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
-                          const void* gate, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, uint32_t flags, void* stream) {
+                          const void* gate, void* out, float* lse, uint32_t flags, bool* done) {
+  *done = false;
   hattn_status st = check_cfg(cfg);
   if (st != HATTN_OK) return st;
   if (B < 0 || cap < 1) return HATTN_ERR_SHAPE;
   if ((flags & ~(uint32_t)HATTN_ROPE_Q_FUSED) != 0) return HATTN_ERR_UNSUPPORTED;
   if (cfg->kind == HATTN_SLIDING && cap != cfg->window) return HATTN_ERR_RANGE;
-  if (B == 0) return HATTN_OK;
+  if (B == 0) {
+    *done = true;
+    return HATTN_OK;
+  }
   if (!q || !k_cache || !v_cache || !pos || !gate || !out) return HATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned2(out) ||
       !aligned2(gate) || !aligned4(pos) || (lse && !aligned4(lse)))
     return HATTN_ERR_ALIGN;
   if (B > 65535 || (long long)B * cap >= (1LL << 40)) return HATTN_ERR_SHAPE;
+  return HATTN_OK;
+}
+
+// The decode's launches on checked arguments and a workspace of at least decode_need bytes.
+hattn_status decode_launch(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                           const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
+                           const void* gate, void* out, float* lse, void* workspace,
+                           uint32_t flags, void* stream) {
   const hattn::DecodePlan plan = hattn::decode_plan(B, decode_max_keys(cfg, cap));
-  const size_t need = decode_need(cfg, B, cap);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
-  if (workspace != nullptr && !aligned16(workspace)) return HATTN_ERR_ALIGN;
   const hattn::RopeTable tab = rope_table(cfg);
   if (cfg->kind == HATTN_SLIDING)
     return hip_status(hattn::launch_ring_decode(
@@ -324,6 +339,70 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
       static_cast<const hattn::bf16_t*>(gate), static_cast<hattn::bf16_t*>(out), lse,
       cfg->kind == HATTN_SLIDING ? cfg->window : 0, (flags & HATTN_ROPE_Q_FUSED) != 0, tab,
       scale_log2e(cfg), plan, workspace, as_stream(stream)));
+}
+
+// Scratch of hattn_decode_noalloc: the split partials (and a sliding ring split's partials
+// and arrival counters) that hattn_decode keeps in the caller's workspace.  Each device
+// the library runs on holds its own copy until the process ends.  Host code never passes
+// this name to a kernel (on the host it is a stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns for the current device, kept in g_scratch.
+constexpr size_t kScratchBytes = HATTN_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The scratch array's address on the calling thread's current device, looked up on the
+// first call on that device (with it current) and kept.
+hattn_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return HATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                          const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
+                          const void* gate, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream) {
+  bool done = false;
+  const hattn_status st =
+      check_decode(cfg, q, k_cache, v_cache, cap, pos, B, gate, out, lse, flags, &done);
+  if (st != HATTN_OK || done) return st;
+  const size_t need = decode_need(cfg, B, cap);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return HATTN_ERR_ALIGN;
+  return decode_launch(cfg, q, k_cache, v_cache, cap, pos, B, gate, out, lse, workspace, flags,
+                       stream);
+}
+
+hattn_status hattn_decode_noalloc(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                                  const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
+                                  const void* gate, void* out, float* lse, uint32_t flags,
+                                  void* stream) {
+  bool done = false;
+  hattn_status st =
+      check_decode(cfg, q, k_cache, v_cache, cap, pos, B, gate, out, lse, flags, &done);
+  if (st != HATTN_OK || done) return st;
+  if (decode_need(cfg, B, cap) > kScratchBytes) return HATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != HATTN_OK) return st;
+  return decode_launch(cfg, q, k_cache, v_cache, cap, pos, B, gate, out, lse, ws, flags, stream);
 }
 
 hattn_status hattn_qkv_proj(const void* x, int32_t T, const void* w_qkv, const void* w_gate,
@@ -363,6 +442,8 @@ const char* hattn_status_string(hattn_status status) {
     case HATTN_ERR_ALIGN: return "tensor pointer not aligned";
     case HATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
     case HATTN_ERR_HIP: return "HIP launch failed";
+    case HATTN_ERR_SCRATCH:
+      return "decode needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

@@ -22,6 +22,8 @@ HATTN_ERR_RANGE = 4
 HATTN_ERR_ALIGN = 5
 HATTN_ERR_WORKSPACE = 6
 HATTN_ERR_HIP = 7
+HATTN_ERR_SCRATCH = 8
+DECODE_NOALLOC_MAX_BYTES = 32 << 20
 HATTN_SLIDING = 0
 HATTN_FULL = 1
 HATTN_ROPE_Q_FUSED = 1
@@ -32,7 +34,8 @@ EXPORTS = ("hattn_cfg_preset", "hattn_rope_qk", "hattn_kv_append", "hattn_kv_app
            "hattn_prefill", "hattn_prefill_ring", "hattn_kv_append_fp8", "hattn_decode_fp8",
            "hattn_decode_fp8_workspace_bytes",
            "hattn_qkv_proj", "hattn_o_proj",
-           "hattn_decode_workspace_bytes", "hattn_decode", "hattn_model_layer_kind",
+           "hattn_decode_workspace_bytes", "hattn_decode", "hattn_decode_noalloc",
+           "hattn_model_layer_kind",
            "hattn_model_kv_bytes", "hattn_model_decode_workspace_bytes", "hattn_model_decode",
            "hattn_model_prefill_workspace_bytes", "hattn_model_prefill",
            "hattn_status_string", "hattn_last_hip_error")
@@ -109,6 +112,8 @@ def _load():
     lib.hattn_decode.argtypes = [cfgp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
                                  ctypes.c_size_t, u32, vp]
     lib.hattn_decode.restype = i32
+    lib.hattn_decode_noalloc.argtypes = [cfgp, vp, vp, vp, i32, vp, i32, vp, vp, vp, u32, vp]
+    lib.hattn_decode_noalloc.restype = i32
     lib.hattn_status_string.argtypes = [i32]
     lib.hattn_status_string.restype = ctypes.c_char_p
     lib.hattn_last_hip_error.argtypes = []
@@ -301,6 +306,24 @@ def decode(cfg: LayerCfg, q, k_cache, v_cache, pos, gate, out, lse=None, workspa
     _check(_lib.hattn_decode(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache), cap,
                              _ptr(pos), B, _ptr(gate), _ptr(out), _ptr(lse), _ptr(workspace),
                              ws_bytes, flags, _stream(stream)), "hattn_decode")
+
+
+def decode_noalloc(cfg: LayerCfg, q, k_cache, v_cache, pos, gate, out, lse=None,
+                   rope_q_fused: bool = False, stream=None):
+    """decode() without a workspace: the library's static per-device scratch holds the
+    partials (calls that overlap on one GPU race on it)."""
+    a = _Args("decode_noalloc")
+    B = int(q.shape[0])
+    a("q", q, _BF16, (B, 1, 16, 256))
+    a("k_cache", k_cache, _BF16, (B, None, 4, 256))
+    a("v_cache", v_cache, _BF16, tuple(k_cache.shape))
+    a("pos", pos, _I32, numel=B)
+    _attn_out_args(a, B, 1, gate, out, lse)
+    a.done()
+    flags = HATTN_ROPE_Q_FUSED if rope_q_fused else 0
+    _check(_lib.hattn_decode_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     int(k_cache.shape[1]), _ptr(pos), B, _ptr(gate), _ptr(out),
+                                     _ptr(lse), flags, _stream(stream)), "hattn_decode_noalloc")
 
 
 def alloc_workspace(cfg: LayerCfg, B: int, cap: int, device="cuda"):

@@ -52,7 +52,9 @@ enum {
   HATTN_ERR_RANGE = 4,       /* cap, window or position-range rule broken               */
   HATTN_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned                 */
   HATTN_ERR_WORKSPACE = 6,   /* decode workspace NULL or smaller than required          */
-  HATTN_ERR_HIP = 7          /* a HIP launch failed; hattn_last_hip_error() has the code */
+  HATTN_ERR_HIP = 7,         /* a HIP launch failed; hattn_last_hip_error() has the code */
+  HATTN_ERR_SCRATCH = 8      /* hattn_decode_noalloc: the call needs more scratch than
+                                HATTN_DECODE_NOALLOC_MAX_BYTES                        */
 };
 
 /* Layer kinds.  [T1] "Hybrid attention: only one layer in four gets the full view";
@@ -193,6 +195,28 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
                           const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
                           const void* gate, void* out, float* lse, void* workspace,
                           size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* hattn_decode for callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc -- and so cannot pass a
+ * workspace.  Arguments, layouts, arithmetic and results as hattn_decode (the same kernels
+ * and split plan); the partials and counters that hattn_decode keeps in the caller's
+ * workspace go to a static device array of HATTN_DECODE_NOALLOC_MAX_BYTES bytes instead,
+ * which each GPU the library runs on holds until the process ends.  The call allocates
+ * nothing (no hipMalloc, no library routine that allocates).  Its first call on a device
+ * looks up that device's copy of the array (the calling thread's current device, which
+ * must be the device of `stream` and of the buffers) and keeps its address.
+ *   HATTN_ERR_SCRATCH: hattn_decode_workspace_bytes(cfg, B, cap) exceeds
+ *     HATTN_DECODE_NOALLOC_MAX_BYTES (a full layer at B up to about 2000 fits); nothing is
+ *     enqueued.  Other errors as hattn_decode.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind; each call
+ * clears what must start at zero.  Calls that overlap on one GPU (on different streams, or
+ * from different host threads without ordering) race on the array and give wrong
+ * results: order them on one stream. */
+#define HATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+hattn_status hattn_decode_noalloc(const hattn_layer_cfg* cfg, const void* q, const void* k_cache,
+                                  const void* v_cache, int32_t cap, const int32_t* pos, int32_t B,
+                                  const void* gate, void* out, float* lse, uint32_t flags,
+                                  void* stream);
 
 /* ---- 8-bit KV cache ------------------------------------------------------------------
  * The library's own 8-bit cache format (for the quantized KV cache the pages' 1M

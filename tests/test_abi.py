@@ -49,7 +49,7 @@ def test_presets(h):
 def test_status_strings(h):
     lib = h.lib()
     seen = set()
-    for st in range(8):
+    for st in range(9):
         s = lib.hattn_status_string(st).decode()
         assert s and s not in seen
         seen.add(s)
@@ -367,3 +367,31 @@ def test_binding_rejects_wrong_tensors_before_the_abi(h):
                    k_cache=K, v_cache=K, out=out[:, :1].contiguous(), lse=None)]
     raises(h.model_decode, layers, cap, pos, torch.zeros(16, dtype=torch.uint8),
            match="layer 0 k_cache must have shape")      # layer 0 is sliding: a 512-slot ring
+
+
+def test_decode_noalloc_validation(h):
+    """The allocation-free decode rejects what hattn_decode rejects, with the same codes,
+    and a request beyond its static scratch with HATTN_ERR_SCRATCH, all before any launch
+    (no GPU needed)."""
+    lib = h.lib()
+    f, s = _cfg(h, "full"), _cfg(h, "sliding")
+
+    def call(cfg=f, q=A, k=A, v=A, cap=131136, pos=A, B=32, g=A, out=A, lse=None, flags=0):
+        return lib.hattn_decode_noalloc(cfg, q, k, v, cap, pos, B, g, out, lse, flags, None)
+
+    for kw in ("q", "k", "v", "pos", "g", "out"):
+        assert call(**{kw: None}) == h.HATTN_ERR_NULL, kw
+    assert call(q=MIS) == h.HATTN_ERR_ALIGN
+    assert call(cfg=s, cap=131136) == h.HATTN_ERR_RANGE
+    assert call(flags=2) == h.HATTN_ERR_UNSUPPORTED
+    assert call(B=70000) == h.HATTN_ERR_SHAPE
+    assert call(cap=0) == h.HATTN_ERR_SHAPE
+    assert call(B=0) == h.HATTN_OK
+    # beyond the scratch: 3000 sequences of one 1032-float partial per (KV head, q head)
+    need = lib.hattn_decode_workspace_bytes(f, 3000, 1 << 20)
+    assert need > h.DECODE_NOALLOC_MAX_BYTES
+    assert call(B=3000, cap=1 << 20) == h.HATTN_ERR_SCRATCH
+    assert "scratch" in lib.hattn_status_string(h.HATTN_ERR_SCRATCH).decode()
+    # the largest measured shapes fit
+    assert lib.hattn_decode_workspace_bytes(f, 32, 131136) <= h.DECODE_NOALLOC_MAX_BYTES
+    assert lib.hattn_decode_workspace_bytes(f, 1, (1 << 20) + 64) <= h.DECODE_NOALLOC_MAX_BYTES
