@@ -265,24 +265,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 //   * QK: a lane's K fragment (8 codes of one key) is widened exactly to bf16 with the
 //     hardware conversion (scale 1), the bf16 MFMA runs as before, and the key's scale
 //     multiplies its score: sum_d q_d (c_d s) = s sum_d q_d c_d.
-//   * PV: the value scale of key j is folded into its probability before the broadcast
-//     (sum_j p_j s_j c_j); lane (kq, dg16) accumulates keys kq, kq + 4, .. of the step over
-//     dims 16 dg16 .. +15, and the 4 key phases are summed at the end of the chunk.
+//   * PV on MFMA too: O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, one MFMA per 16 dims.
+//     The value scale of key j is folded into its probability before the broadcast
+//     (sum_j p_j s_j c_j).  Lane (kq = lane / 16, i = lane mod 16) holds the 16 codes of
+//     dims 16 i .. 16 i + 15 of keys kq, kq + 4, .., kq + 28 of the step: that is the V^T
+//     operand of 16 MFMAs, MFMA e covering dims 16 i + e with K-index 8 kq + m being key
+//     kq + 4m.  The codes are widened exactly to bf16 two at a time and one byte permute
+//     pairs a dim of two keys.  The probabilities reach the P^T operand through LDS in that
+//     key order.  This replaced VALU dot products (v_dot2_f32_bf16, 352 VALU operations per
+//     32-key step), which left the kernel bound by VALU issue: 397 -> 377 us at 2^20 keys.
 // The softmax sum uses the unscaled probabilities.  [T5] §3.2 "Deployment steps and key
 // parameters" (quantized KV cache for the 1M context).
 template <bool kSliding>
-__global__ __launch_bounds__(256) void decode_split_fp8_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_split_fp8_kernel(
     const bf16_t* __restrict__ q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const float* __restrict__ ksc, const float* __restrict__ vsc, int cap,
     const int* __restrict__ pos, int window, int chunk, int nchunks, float* __restrict__ ws_o,
     float* __restrict__ ws_ml, int rope_q, RopeTable tab, float sl2) {
   constexpr int kNdc = kSliding ? 4 : 1;
-  __shared__ __attribute__((aligned(16))) float p_lds[kHkv][kStep][4];
+  // Per wave: probability of step key j for head h at [h][8 (j mod 4) + j / 4].
+  __shared__ __attribute__((aligned(16))) float p_lds[kHkv][kGroup][kStep];
 
   const int c = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, kvh = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;    // MFMA view: column (head) and k-group
-  const int kq = lane >> 4, dg = lane & 15;    // PV view: key phase and 16-dim group
+  const int kq = lane >> 4;                    // V load view: key phase and 16-dim group
   const int p = pos[b];
   // Keys 0 .. p (the last window of them on sliding layers), within the cache; formed
   // without p + 1, which overflows at the largest position.
@@ -326,11 +334,10 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
   const float* vs = vsc + ((long long)b * kHkv + kvh) * cap;
 
   float m_run = -INFINITY, l_run = 0.f;
-  float o[kGroup][16];
+  // O^T accumulators: oacc[e][jj] of lane (column n16 = head, g) is dim 16 (4 g + jj) + e.
+  f32x4 oacc[16];
 #pragma unroll
-  for (int hl = 0; hl < kGroup; ++hl)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[hl][e] = 0.f;
+  for (int e = 0; e < 16; ++e) oacc[e] = f32x4{};
 
   // Step k0's K codes, scales and V codes.  Keys past k_end read row k_end - 1 (masked
   // scores, zero probabilities), so the loads are unconditional and the compiler can count
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = min(k0 + kq + 4 * i, k_end - 1);
-      vraw[i] = *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 16 * dg);
+      vraw[i] = *reinterpret_cast<const uint4*>(vb + (long long)key * rs + 16 * n16);
     }
   };
   if (k_begin < k_end) {
@@ -406,18 +413,9 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      // Per-head factors live in lanes 0..3 (column = head, k-group 0).
-      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-      const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
-      const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
-      const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+      // Each lane's accumulators belong to its own column (head), whose factor it holds.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        o[0][e] *= a0;
-        o[1][e] *= a1;
-        o[2][e] *= a2;
-        o[3][e] *= a3;
-      }
+      for (int e = 0; e < 16; ++e) oacc[e] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rsum = 0.f;
@@ -436,60 +434,63 @@ __global__ __launch_bounds__(256) void decode_split_fp8_kernel(
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          p_lds[kvh][16 * blk + 4 * g + j][n16] = sv[blk][j] * vsc[blk][j];
+          p_lds[kvh][n16][8 * j + 4 * blk + g] = sv[blk][j] * vsc[blk][j];
     }
     wave_lds_fence();
-    // Keys a = kq + 8j and b = a + 4 share a lane: a byte permute interleaves their codes,
-    // one conversion yields the (a, b) pair of a dim in bf16, and one dot2 adds p_a v_a +
-    // p_b v_b (probabilities, with the V scales folded in, in bf16).
+    // P^T operand: lane (column n16, k-group g) takes K-indices 8g .. 8g + 7, i.e. keys g,
+    // g + 4, .., g + 28, at slots 8g .. 8g + 7 (columns past the 4 heads read a head's
+    // row; those output columns are never stored).
+    bf16x8 pf;
+    {
+      const float* prow = &p_lds[kvh][n16 & (kGroup - 1)][8 * g];
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(prow);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(prow + 4);
+      const bf16x4 lo = __builtin_convertvector(pa, bf16x4), hi = __builtin_convertvector(pb, bf16x4);
+      pf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    // V^T operand of MFMA e = 4w + 2hf + bs: element m (K-index 8 kq + m) is dim 16 dg + e
+    // of key kq + 4m, code byte e of vraw[m].  Each code word is widened to two bf16 pairs
+    // (dims 4w, 4w + 1 and 4w + 2, 4w + 3 of one key); a permute then pairs one dim of keys
+    // 2t and 2t + 1.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 pa = *reinterpret_cast<const f32x4*>(&p_lds[kvh][kq + 8 * j][0]);
-      const f32x4 pb = *reinterpret_cast<const f32x4*>(&p_lds[kvh][kq + 8 * j + 4][0]);
-      bf16x2 pp[kGroup];
+    for (int w = 0; w < 4; ++w) {
+      uint32_t x[8][2];
 #pragma unroll
-      for (int hl = 0; hl < kGroup; ++hl) pp[hl] = __builtin_bit_cast(bf16x2, pack_bf16x2(pa[hl], pb[hl]));
-      const uint32_t va[4] = {vraw[2 * j].x, vraw[2 * j].y, vraw[2 * j].z, vraw[2 * j].w};
-      const uint32_t vb2[4] = {vraw[2 * j + 1].x, vraw[2 * j + 1].y, vraw[2 * j + 1].z, vraw[2 * j + 1].w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = __builtin_amdgcn_perm(vb2[w], va[w], 0x05010400u);  // a0 b0 a1 b1
-        const uint32_t hi = __builtin_amdgcn_perm(vb2[w], va[w], 0x07030602u);  // a2 b2 a3 b3
-        const bf16x2 d[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false),
-                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true),
-                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false),
-                             __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int hl = 0; hl < kGroup; ++hl)
-            o[hl][4 * w + e] = __builtin_amdgcn_fdot2_f32_bf16(d[e], pp[hl], o[hl][4 * w + e], false);
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t d = w == 0 ? vraw[m].x : w == 1 ? vraw[m].y : w == 2 ? vraw[m].z : vraw[m].w;
+        x[m][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, false));
+        x[m][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, true));
       }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int bs = 0; bs < 2; ++bs) {
+          const uint32_t sel = bs ? 0x07060302u : 0x05040100u;  // high or low bf16 of each
+          const uint32_t a0 = __builtin_amdgcn_perm(x[1][hf], x[0][hf], sel);
+          const uint32_t a1 = __builtin_amdgcn_perm(x[3][hf], x[2][hf], sel);
+          const uint32_t a2 = __builtin_amdgcn_perm(x[5][hf], x[4][hf], sel);
+          const uint32_t a3 = __builtin_amdgcn_perm(x[7][hf], x[6][hf], sel);
+          const int e = 4 * w + 2 * hf + bs;
+          oacc[e] = mfma16(__builtin_bit_cast(bf16x8, uint4{a0, a1, a2, a3}), pf, oacc[e]);
+        }
     }
     load_v(kn);
     wave_lds_fence();
   }
 
-  // Sum the 4 key phases, then the softmax sums over the 4 k-groups.
-#pragma unroll
-  for (int hl = 0; hl < kGroup; ++hl)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      o[hl][e] += __shfl_xor(o[hl][e], 16);
-      o[hl][e] += __shfl_xor(o[hl][e], 32);
-    }
+  // The softmax sums over the 4 k-groups.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
   const long long part = ((long long)(b * kHkv + kvh) * nchunks + c) * kGroup;
-  if (kq == 0) {
+  if (qlane) {
 #pragma unroll
-    for (int hl = 0; hl < kGroup; ++hl) {
-      float* dst = ws_o + (part + hl) * kD + 16 * dg;
+    for (int jj = 0; jj < 4; ++jj) {
+      float* dst = ws_o + (part + n16) * kD + 16 * (4 * g + jj);
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4)
         *reinterpret_cast<f32x4*>(dst + 4 * e4) =
-            f32x4{o[hl][4 * e4], o[hl][4 * e4 + 1], o[hl][4 * e4 + 2], o[hl][4 * e4 + 3]};
+            f32x4{oacc[4 * e4][jj], oacc[4 * e4 + 1][jj], oacc[4 * e4 + 2][jj], oacc[4 * e4 + 3][jj]};
     }
   }
   if (lane < kGroup) {
