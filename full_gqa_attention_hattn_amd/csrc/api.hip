@@ -70,8 +70,7 @@ int decode_max_keys(const hattn_layer_cfg* cfg, int32_t cap) {
 }
 
 // Workspace a decode needs: full layers, the split-KV partials; sliding layers, the ring
-// split's partials and counters at B <= 2 and nothing above (no partial leaves a
-// workgroup there).
+// split's partials and counters.
 size_t decode_need(const hattn_layer_cfg* cfg, int32_t B, int32_t cap) {
   if (cfg->kind == HATTN_SLIDING) return hattn::ring_step_workspace_bytes(B);
   return hattn::decode_workspace_bytes(B, hattn::decode_plan(B, decode_max_keys(cfg, cap)));

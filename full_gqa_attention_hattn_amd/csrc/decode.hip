@@ -26,6 +26,11 @@ namespace hattn {
 namespace {
 
 constexpr int kStep = 32;  // keys per wave step
+// Cache policy of a device-scope buffer access (the SC1 bit): stores are written through
+// to, and loads read from, the level that all XCDs share.
+constexpr int kScDevice = 16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kRescaleLog2 = 8.f;  // move the reference max only when beaten by 2^8
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -571,322 +576,34 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
 }
 
-constexpr int kRingWaves = 4;  // waves of the fused ring step
+constexpr int kRingSlots = 512;  // a sliding layer's ring
 
-// One decode step of a sliding layer in a single launch: append, attention over the ring
-// and the merge.  Workgroup (kv head, b) rotates the new key by the token's position p and
-// writes K and V to ring slot p mod 512 (the same bits as the rotating append), then
-// attends query heads 4 kvh .. 4 kvh + 3 over the ring's min(p + 1, 512) filled slots: each
-// of the 4 waves takes 128 slots (four of the split kernel's steps), and the 4 partials are
-// merged by log-sum-exp through LDS, normalised, gated and stored as the combine does.
-// The cos/sin of p * omega_i are computed once and serve both the key and the query.
+// Workgroups per (sequence, KV head) of the ring kernel for B sequences.  Measured per
+// call inside a captured graph, cold rings: 8 splits of 2 waves are fastest up to B = 8
+// (10.1 us at B = 1, 11.6 at 8), 4 of 4 waves above (13.6 us at 16, 19.9 at 32, where
+// 8 splits took 22.5).  One workgroup per (sequence, KV head), or one per pair of query
+// heads reading the whole ring, took 17.0 us at B = 1 and 21.4 at 32: a CU alone
+// streams only ~37 B/clk, so a head's 512 KiB ring has to spread over several.
+int ring_splits(int B) { return B <= 8 ? 8 : 4; }
+
+// Attention over a sliding layer's ring in one launch, for any batch: the 512 slots of
+// each (sequence, KV head) are split over kRingSplits workgroups of kSplitWaves waves, one
+// 32-slot step per wave.  Each wave issues its slots' loads first, before the position
+// is known (every slot is addressable; unfilled ones are masked afterwards, their values
+// zeroed so that NaN contents never reach the sum).  Every workgroup computes cos / sin
+// of p * omega_i; with kAppend, the one whose slots hold p mod 512 rotates the new key by
+// p and writes K and V to that slot (the same bits as the rotating append), and the lanes
+// holding that slot take it from LDS.  Each workgroup attends query heads 4 kvh ..
+// 4 kvh + 3, merges its waves through LDS and publishes the partial (reference max, sum,
+// unnormalised o) to the workspace with device-scope stores.  The last workgroup to
+// arrive (a counter per (sequence, KV head), which it resets to zero) merges the
+// kRingSplits partials by log-sum-exp, normalises, gates and stores as the combine does.
 // [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
 // tokens); [T3] "Sliding window 512" (RoPE theta 1e4 over all 256 dims).
 // kAppend: the step's append is fused in (the schedule driver); otherwise the token's key
 // and value are already in the ring (a plain sliding decode), and rope_q says whether q
 // still needs its rotation.
-template <bool kAppend>
-__global__ __launch_bounds__(64 * kRingWaves) void ring_step_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
-    const bf16_t* __restrict__ v_new, bf16_t* __restrict__ k_ring, bf16_t* __restrict__ v_ring,
-    const int* __restrict__ pos, const bf16_t* __restrict__ gate, bf16_t* __restrict__ out,
-    float* __restrict__ lse, RopeTable tab, float sl2, int rope_q) {
-  constexpr int kSlots = 512;
-  constexpr int kHalf = 128;       // rot_dim / 2
-  constexpr int kPerWave = kSlots / kRingWaves;
-  __shared__ f32x2 cs[kHalf];
-  __shared__ __attribute__((aligned(16))) float p_lds[kRingWaves][kStep][4];
-  __shared__ __attribute__((aligned(16))) float part_o[kRingWaves][kGroup][kD];
-  __shared__ float part_ml[kRingWaves][kGroup][2];
-
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n16 = lane & 15, g = lane >> 4;
-  const int half = lane >> 5, dg = lane & 31;
-  const int p = pos[b];
-
-  // The query's loads go out first; the append and its fence hide their latency.
-  const bool qlane = n16 < kGroup;
-  bf16x8 qf[8];
-  {
-    const bf16_t* qrow = q + ((long long)b * kHq + kvh * kGroup + (qlane ? n16 : 0)) * kD + 8 * g;
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc)
-      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
-  }
-
-  if (tid < kHalf && (kAppend || rope_q)) {
-    float sv, cv;
-    sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
-    cs[tid] = f32x2{cv, sv};
-  }
-  __syncthreads();
-
-  const long long ring_off = ((long long)b * kSlots * kHkv + kvh) * kD;
-  if (kAppend && p >= 0) {
-    const long long row = ring_off + (long long)(p & (kSlots - 1)) * kHkv * kD;
-    const long long src = ((long long)b * kHkv + kvh) * kD;
-    if (tid < kHalf / 8) {
-      // Dims d0 .. d0 + 7 and their partners d0 + 128 .. d0 + 135.
-      const int d0 = 8 * tid;
-      const uint4 xa = *reinterpret_cast<const uint4*>(k_new + src + d0);
-      const uint4 xb = *reinterpret_cast<const uint4*>(k_new + src + d0 + kHalf);
-      const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
-      const uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
-      uint32_t ya[4], yb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f32x2 c0 = cs[d0 + 2 * e], c1 = cs[d0 + 2 * e + 1];
-        float ya0, yb0, ya1, yb1;
-        rope_pair(bf16_lo(wa[e]), bf16_lo(wb[e]), c0.x, c0.y, &ya0, &yb0);
-        rope_pair(bf16_hi(wa[e]), bf16_hi(wb[e]), c1.x, c1.y, &ya1, &yb1);
-        ya[e] = pack_bf16x2(ya0, ya1);
-        yb[e] = pack_bf16x2(yb0, yb1);
-      }
-      *reinterpret_cast<uint4*>(k_ring + row + d0) = uint4{ya[0], ya[1], ya[2], ya[3]};
-      *reinterpret_cast<uint4*>(k_ring + row + d0 + kHalf) = uint4{yb[0], yb[1], yb[2], yb[3]};
-    } else if (tid < kHalf / 8 + kD / 8) {
-      const int d0 = 8 * (tid - kHalf / 8);
-      *reinterpret_cast<uint4*>(v_ring + row + d0) = *reinterpret_cast<const uint4*>(v_new + src + d0);
-    }
-  }
-  // The new row is read below by other waves of this workgroup only: the barrier's
-  // workgroup-scope release and acquire make it visible (the waves share one CU), with no
-  // device-scope fence, which would write back and invalidate L2.
-  __syncthreads();
-
-  // Q^T operand as in the split kernel (loaded first, above), rotated with the shared table.
-  if (qlane && rope_q) {
-#pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      const bf16x8 xa = qf[dc], xb = qf[dc + 4];
-      f32x4 ya0, ya1, yb0, yb1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f32x2 c = cs[32 * dc + 8 * g + e];
-        float ya, yb;
-        rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
-        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
-      }
-      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
-      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
-      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      qf[dc + 4] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    }
-  }
-
-  const int kv_len = p >= 0 ? min(p, kSlots - 1) + 1 : 0;  // no p + 1: p may be 2^31 - 1
-  const int k_begin = kPerWave * w;
-  const int k_end = min(kv_len, k_begin + kPerWave);
-  float m_run = -INFINITY, l_run = 0.f;
-  float o[kGroup][8];
-#pragma unroll
-  for (int hl = 0; hl < kGroup; ++hl)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
-  attend_keys(qf, k_ring + ring_off, v_ring + ring_off, k_begin, k_end, sl2, p_lds[w], lane,
-              m_run, l_run, o);
-#pragma unroll
-  for (int hl = 0; hl < kGroup; ++hl)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hl][e] += __shfl_xor(o[hl][e], 32);
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (half == 0) {
-#pragma unroll
-    for (int hl = 0; hl < kGroup; ++hl) {
-      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg]) = f32x4{o[hl][0], o[hl][1], o[hl][2], o[hl][3]};
-      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg + 4]) = f32x4{o[hl][4], o[hl][5], o[hl][6], o[hl][7]};
-    }
-  }
-  if (lane < kGroup) {
-    part_ml[w][lane][0] = m_run;
-    part_ml[w][lane][1] = l_run;
-  }
-  __syncthreads();
-
-  // Merge: thread (head hl, dims 4j .. 4j + 3).
-  const int hl = tid >> 6, d = 4 * (tid & 63);
-  float M = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < kRingWaves; ++v) M = fmaxf(M, part_ml[v][hl][0]);
-  const float M_use = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  f32x4 acc = f32x4{};
-#pragma unroll
-  for (int v = 0; v < kRingWaves; ++v) {
-    const float wgt = fast_exp2(part_ml[v][hl][0] - M_use);
-    L += part_ml[v][hl][1] * wgt;
-    acc += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d]) * wgt;
-  }
-  const long long row = (long long)b * kHq + kvh * kGroup + hl;
-  const float gl = bf16_to_f32(gate[row]);
-  const float sg = 1.f / (1.f + expf(-gl));
-  const float f = L > 0.f ? sg / L : 0.f;
-  *reinterpret_cast<uint2*>(out + row * kD + d) =
-      uint2{pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f)};
-  if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-}
-
-// Sliding decode above two sequences (the token's key and value already in the ring):
-// the query heads of each (sequence, KV head) are split over kGroup / NH workgroups, each
-// attending NH heads over the whole ring with kW waves of 512 / kW slots.  No partial
-// crosses workgroups, so there is no merge between them; the ring rows are read once per
-// workgroup, and the workgroups of one (sequence, KV head) run on one XCD (workgroup i
-// runs on XCD i mod 8), where the second read of those rows hits that XCD's L2.  At
-// B = 32 that fills the chip with 256 workgroups, where one workgroup per (sequence, KV
-// head) left half the CUs idle and ran each wave's four steps one after another.
-// [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
-// tokens); [T3] "Sliding window 512"; [T1] "GQA, fused projection and output gating".
-template <int NH, int kW>
-__global__ __launch_bounds__(64 * kW) void ring_heads_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_ring,
-    const bf16_t* __restrict__ v_ring, const int* __restrict__ pos, int B,
-    const bf16_t* __restrict__ gate, bf16_t* __restrict__ out, float* __restrict__ lse,
-    RopeTable tab, float sl2, int rope_q) {
-  constexpr int kSlots = 512;
-  constexpr int kHalf = 128;                 // rot_dim / 2
-  constexpr int kSplit = kGroup / NH;        // workgroups per (sequence, KV head)
-  constexpr int kPerWave = kSlots / kW;      // ring slots per wave
-  static_assert(kGroup % NH == 0 && kPerWave % kStep == 0, "ring split shape");
-  static_assert(64 * kW >= kHalf && 64 * kW >= 64 * NH, "table and merge thread counts");
-  __shared__ f32x2 cs[kHalf];
-  __shared__ __attribute__((aligned(16))) float p_lds[kW][kStep][4];
-  __shared__ __attribute__((aligned(16))) float part_o[kW][NH][kD];
-  __shared__ float part_ml[kW][NH][2];
-
-  // Workgroup id -> (XCD, j): the kSplit workgroups of (sequence, KV head) `grp` are
-  // ids 8 (kSplit g' + part) + xcd with grp = 8 g' + xcd, all on XCD xcd.
-  const int id = (int)blockIdx.x, xcd = id & 7, j = id >> 3;
-  const int part = j % kSplit;
-  const int grp = (j / kSplit) * 8 + xcd;
-  if (grp >= B * kHkv) return;
-  const int b = grp / kHkv, kvh = grp % kHkv;
-  const int h0 = kvh * kGroup + part * NH;   // first query head of this workgroup
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n16 = lane & 15, g = lane >> 4;
-  const int half = lane >> 5, dg = lane & 31;
-  const int p = pos[b];
-
-  const bool qlane = n16 < NH;
-  bf16x8 qf[8];
-  {
-    const bf16_t* qrow = q + ((long long)b * kHq + h0 + (qlane ? n16 : 0)) * kD + 8 * g;
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc)
-      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
-  }
-  if (rope_q) {
-    if (tid < kHalf) {
-      float sv, cv;
-      sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
-      cs[tid] = f32x2{cv, sv};
-    }
-    __syncthreads();
-    if (qlane) {
-#pragma unroll
-      for (int dc = 0; dc < 4; ++dc) {
-        const bf16x8 xa = qf[dc], xb = qf[dc + 4];
-        f32x4 ya0, ya1, yb0, yb1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const f32x2 c = cs[32 * dc + 8 * g + e];
-          float ya, yb;
-          rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
-          if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
-        }
-        const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
-        const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
-        qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        qf[dc + 4] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      }
-    }
-  }
-
-  const long long ring_off = ((long long)b * kSlots * kHkv + kvh) * kD;
-  const int kv_len = p >= 0 ? min(p, kSlots - 1) + 1 : 0;  // no p + 1: p may be 2^31 - 1
-  const int k_begin = kPerWave * w;
-  const int k_end = min(kv_len, k_begin + kPerWave);
-  float m_run = -INFINITY, l_run = 0.f;
-  float o[NH][8];
-#pragma unroll
-  for (int hl = 0; hl < NH; ++hl)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hl][e] = 0.f;
-  attend_keys<NH>(qf, k_ring + ring_off, v_ring + ring_off, k_begin, k_end, sl2, p_lds[w], lane,
-                  m_run, l_run, o);
-#pragma unroll
-  for (int hl = 0; hl < NH; ++hl)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[hl][e] += __shfl_xor(o[hl][e], 32);
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (half == 0) {
-#pragma unroll
-    for (int hl = 0; hl < NH; ++hl) {
-      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg]) = f32x4{o[hl][0], o[hl][1], o[hl][2], o[hl][3]};
-      *reinterpret_cast<f32x4*>(&part_o[w][hl][8 * dg + 4]) = f32x4{o[hl][4], o[hl][5], o[hl][6], o[hl][7]};
-    }
-  }
-  if (lane < NH) {
-    part_ml[w][lane][0] = m_run;
-    part_ml[w][lane][1] = l_run;
-  }
-  __syncthreads();
-
-  // Merge the kW wave partials: thread (head hl, dims 4i .. 4i + 3).
-  if (tid >= 64 * NH) return;
-  const int hl = tid >> 6, d = 4 * (tid & 63);
-  float M = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < kW; ++v) M = fmaxf(M, part_ml[v][hl][0]);
-  const float M_use = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  f32x4 acc = f32x4{};
-#pragma unroll
-  for (int v = 0; v < kW; ++v) {
-    const float wgt = fast_exp2(part_ml[v][hl][0] - M_use);
-    L += part_ml[v][hl][1] * wgt;
-    acc += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d]) * wgt;
-  }
-  const long long row = (long long)b * kHq + h0 + hl;
-  const float gl = bf16_to_f32(gate[row]);
-  const float sg = 1.f / (1.f + expf(-gl));
-  const float f = L > 0.f ? sg / L : 0.f;
-  *reinterpret_cast<uint2*>(out + row * kD + d) =
-      uint2{pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f)};
-  if (d == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-}
-
-constexpr int kHeadsNH = 2;      // query heads per head-split ring workgroup
-constexpr int kHeadsWaves = 8;   // its waves (64 ring slots each)
-
-constexpr int kRingSlots = 512;                     // a sliding layer's ring
-constexpr int kRingSplits = 8;                      // workgroups per (KV head, sequence)
-constexpr int kSplitWaves = 2;                      // waves per split workgroup
-constexpr int kRingPerSplit = kRingSlots / kRingSplits;
-constexpr int kRingSplitMaxB = 2;                   // larger batches use the fused kernel
-static_assert(kRingPerSplit == kSplitWaves * kStep, "one 32-key step per wave");
-
-// The same step for small batches, where one workgroup per (KV head, sequence) leaves most
-// CUs idle: append, attention over the ring and the merge in one launch, with the ring's
-// 512 slots split over kRingSplits workgroups per (KV head,
-// sequence), so that the 512 KiB a head's ring holds stream through that many CUs: one CU
-// alone reached only ~37 B/clk of it.  Every workgroup computes cos / sin of p * omega_i;
-// the one whose slots hold p mod 512 rotates the new key by the token's position p and
-// writes K and V to that slot (the same bits as the rotating append), and only it reads
-// that slot.  Each workgroup attends query heads 4 kvh .. 4 kvh + 3 over its filled slots
-// (one 32-key step per wave), merges its two waves through LDS and publishes the partial
-// (reference max, sum, unnormalised o) to the workspace.  The last workgroup to arrive
-// (a counter per (KV head, sequence), which it resets to zero) merges the kRingSplits
-// partials by log-sum-exp, normalises, gates and stores as the combine does.
-// [T2] "The real bottleneck of a million-token context" (sliding layers keep the last 512
-// tokens); [T3] "Sliding window 512" (RoPE theta 1e4 over all 256 dims).
-// kAppend: the step's append is fused in (the schedule driver); otherwise the token's key
-// and value are already in the ring (a plain sliding decode), and rope_q says whether q
-// still needs its rotation.
-template <bool kAppend>
+template <bool kAppend, int kRingSplits, int kSplitWaves>
 __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
     const bf16_t* __restrict__ v_new, bf16_t* __restrict__ k_ring, bf16_t* __restrict__ v_ring,
@@ -894,10 +611,14 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
     float* __restrict__ lse, RopeTable tab, float sl2, float* __restrict__ ws_o,
     float* __restrict__ ws_ml, unsigned* __restrict__ counters, int rope_q) {
   constexpr int kHalf = 128;       // rot_dim / 2
+  constexpr int kRingPerSplit = kRingSlots / kRingSplits;
+  static_assert(kRingPerSplit == kSplitWaves * kStep, "one 32-key step per wave");
+  static_assert(64 * kSplitWaves >= kHalf / 8 + kD / 8, "append threads");
   __shared__ f32x2 cs[kHalf];
   __shared__ __attribute__((aligned(16))) float p_lds[kSplitWaves][kStep][4];
   __shared__ __attribute__((aligned(16))) float part_o[kSplitWaves][kGroup][kD];
   __shared__ float part_ml[kSplitWaves][kGroup][2];
+  __shared__ uint4 new_k[kD / 8], new_v[kD / 8];   // the appended row, 8 dims per entry
   __shared__ unsigned last;
 
   const int kvh = blockIdx.x / kRingSplits, sp = blockIdx.x % kRingSplits, b = blockIdx.y;
@@ -905,38 +626,68 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
   const int n16 = lane & 15, g = lane >> 4;
   const int half = lane >> 5, dg = lane & 31;
   const int p = pos[b];
-  // Merge threads: head hl, dims d0 .. d0 + 7.
-  const int hl = tid >> 5, d0 = 8 * (tid & 31);
+  // Merge threads (the first 32 kGroup): head hl, dims d0 .. d0 + 7.
+  static_assert(64 * kSplitWaves >= 32 * kGroup, "a merge thread per 8 dims of each head");
+  const bool mt = tid < 32 * kGroup;
+  const int hl = (tid >> 5) & (kGroup - 1), d0 = 8 * (tid & 31);
   const long long row = (long long)b * kHq + kvh * kGroup + hl;
   const float gate_logit = bf16_to_f32(gate[row]);
+  // Read before the ring's loads go out (a dynamically indexed kernel argument is a memory
+  // load, and waiting for it must not wait for them).
+  static_assert(64 * kSplitWaves >= kHalf, "one thread per frequency");
+  const float inv_freq = tab.inv_freq[tid & (kHalf - 1)];
 
+  // Q^T operand: lanes n16 >= 4 load head 0 again (unconditional loads, so that no
+  // branch around a load makes the wave wait for it); their S^T columns repeat head 0's
+  // and nothing reads them.
   const bool qlane = n16 < kGroup;
   bf16x8 qf[8];
   {
     const bf16_t* qrow = q + ((long long)b * kHq + kvh * kGroup + (qlane ? n16 : 0)) * kD + 8 * g;
 #pragma unroll
-    for (int dc = 0; dc < 8; ++dc)
-      qf[dc] = qlane ? *reinterpret_cast<const bf16x8*>(qrow + 32 * dc) : bf16x8{};
+    for (int dc = 0; dc < 8; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qrow + 32 * dc);
   }
+  // The token's key (threads 0 .. 15: dims 8t .. 8t + 7 and their partners 8t + 128 ..)
+  // and value (threads 16 .. 47: dims 8 (t - 16) ..), loaded whichever workgroup appends.
+  const long long src = ((long long)b * kHkv + kvh) * kD;
+  uint4 xa = uint4{}, xb = uint4{};
+  if (kAppend) {
+    // Unconditional too: every thread reads an in-range entry, threads 48 .. drop theirs.
+    const int t = tid & 63;
+    const bf16_t* ks = k_new + src + 8 * (t & (kHalf / 8 - 1));
+    const bf16_t* vs = v_new + src + 8 * ((t - kHalf / 8) & (kD / 8 - 1));
+    const uint4 ka = *reinterpret_cast<const uint4*>(ks);
+    const uint4 kb2 = *reinterpret_cast<const uint4*>(ks + kHalf);
+    const uint4 va = *reinterpret_cast<const uint4*>(vs);
+    xa = t < kHalf / 8 ? ka : va;
+    xb = kb2;
+  }
+  // This wave's 32 slots go out next, before the position is known: every slot of the
+  // ring is addressable, and what the position rules out is masked once it is known.  The
+  // loads above stay ahead of them (the memory counter is waited on in issue order).
+  __builtin_amdgcn_sched_barrier(0);
+  const long long ring_off = ((long long)b * kRingSlots * kHkv + kvh) * kD;
+  const int k_begin = kRingPerSplit * sp + kStep * w;
+  StepRegs r;
+  load_step(r, k_ring + ring_off, v_ring + ring_off, k_begin, k_begin + kStep, lane);
+  __builtin_amdgcn_sched_barrier(0);
 
-  static_assert(64 * kSplitWaves >= kHalf, "one thread per frequency");
-  if (tid < kHalf && (kAppend || rope_q)) {
+  {
+    // Every thread evaluates it (no branch for the frequency's load to sink into).
     float sv, cv;
-    sincos_angle(rope_angle(p, tab.inv_freq[tid]), &sv, &cv);
-    cs[tid] = f32x2{cv, sv};
+    sincos_angle(rope_angle(p, inv_freq), &sv, &cv);
+    if (tid < kHalf && (kAppend || rope_q)) cs[tid] = f32x2{cv, sv};
   }
   __syncthreads();
 
-  const long long ring_off = ((long long)b * kRingSlots * kHkv + kvh) * kD;
   const int slot_new = p & (kRingSlots - 1);
-  if (kAppend && p >= 0 && slot_new / kRingPerSplit == sp) {
+  const bool appends = kAppend && p >= 0 && slot_new / kRingPerSplit == sp;
+  if (appends) {
+    // Rotate the key by p and write K and V to slot p mod 512 (the same bits as the
+    // rotating append), and keep the row in LDS for the lanes that hold that slot.
     const long long dst = ring_off + (long long)slot_new * kHkv * kD;
-    const long long src = ((long long)b * kHkv + kvh) * kD;
     if (tid < kHalf / 8) {
-      // Dims d0 .. d0 + 7 and their partners d0 + 128 .. d0 + 135.
       const int d = 8 * tid;
-      const uint4 xa = *reinterpret_cast<const uint4*>(k_new + src + d);
-      const uint4 xb = *reinterpret_cast<const uint4*>(k_new + src + d + kHalf);
       const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w};
       const uint32_t wb[4] = {xb.x, xb.y, xb.z, xb.w};
       uint32_t ya[4], yb[4];
@@ -949,19 +700,21 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
         ya[e] = pack_bf16x2(ya0, ya1);
         yb[e] = pack_bf16x2(yb0, yb1);
       }
-      *reinterpret_cast<uint4*>(k_ring + dst + d) = uint4{ya[0], ya[1], ya[2], ya[3]};
-      *reinterpret_cast<uint4*>(k_ring + dst + d + kHalf) = uint4{yb[0], yb[1], yb[2], yb[3]};
+      const uint4 ka = uint4{ya[0], ya[1], ya[2], ya[3]}, kb2 = uint4{yb[0], yb[1], yb[2], yb[3]};
+      *reinterpret_cast<uint4*>(k_ring + dst + d) = ka;
+      *reinterpret_cast<uint4*>(k_ring + dst + d + kHalf) = kb2;
+      new_k[tid] = ka;
+      new_k[tid + kHalf / 8] = kb2;
     } else if (tid < kHalf / 8 + kD / 8) {
-      const int d = 8 * (tid - kHalf / 8);
-      *reinterpret_cast<uint4*>(v_ring + dst + d) = *reinterpret_cast<const uint4*>(v_new + src + d);
+      const int e = tid - kHalf / 8;
+      *reinterpret_cast<uint4*>(v_ring + dst + 8 * e) = xa;
+      new_v[e] = xa;
     }
-    // The new row is read below by this workgroup only: the barrier's workgroup-scope
-    // release and acquire make it visible (its waves share one CU).
     __syncthreads();
   }
 
-  // Q^T operand as in the split kernel (loaded first, above), rotated with the shared table.
-  if (qlane && rope_q) {
+  // Q^T rotated with the shared table (every lane, so that the repeats stay head 0's).
+  if (rope_q) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       const bf16x8 xa = qf[dc], xb = qf[dc + 4];
@@ -983,16 +736,42 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
   // Slots [k_begin, k_end) of this wave: the ring's first min(p + 1, 512) slots are filled
   // (formed without p + 1, which overflows at the largest position).
   const int kv_len = p >= 0 ? min(p, kRingSlots - 1) + 1 : 0;
-  const int k_begin = kRingPerSplit * sp + kStep * w;
   const int k_end = min(kv_len, k_begin + kStep);
+  if (k_end < k_begin + kStep) {
+    // Unfilled slots may hold anything (NaN included): their scores are masked to -inf,
+    // and their values are zeroed so that a zero probability meets a zero.
+#pragma unroll
+    for (int kp = 0; kp < 16; ++kp)
+      if (k_begin + 2 * kp + half >= k_end) r.vv[kp] = uint4{0u, 0u, 0u, 0u};
+  }
+  if (appends && (unsigned)(slot_new - k_begin) < (unsigned)kStep) {
+    // The lanes holding the new slot take it from LDS (their loads went out before it
+    // was written).  MFMA view: lane (n16, g) holds dims 8g + 32dc .. of key
+    // k_begin + 16 blk + n16; PV view: lane (half, dg) holds dims 8dg .. of key
+    // k_begin + 2kp + half.
+    const int j = slot_new - k_begin;
+    if (n16 == (j & 15)) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        if (blk == (j >> 4)) {
+#pragma unroll
+          for (int dc = 0; dc < 8; ++dc) r.kf[blk][dc] = __builtin_bit_cast(bf16x8, new_k[g + 4 * dc]);
+        }
+    }
+    if (half == (j & 1)) {
+#pragma unroll
+      for (int kp = 0; kp < 16; ++kp)
+        if (kp == (j >> 1)) r.vv[kp] = new_v[dg];
+    }
+  }
   float m_run = -INFINITY, l_run = 0.f;
   float o[kGroup][8];
 #pragma unroll
   for (int h = 0; h < kGroup; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  attend_keys(qf, k_ring + ring_off, v_ring + ring_off, k_begin, k_end, sl2, p_lds[w], lane,
-              m_run, l_run, o);
+  if (k_end > k_begin)
+    compute_step(r, qf, k_begin, k_end, sl2, p_lds[w], lane, m_run, l_run, o);
 #pragma unroll
   for (int h = 0; h < kGroup; ++h)
 #pragma unroll
@@ -1012,9 +791,17 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
   }
   __syncthreads();
 
+  // The partials of this (sequence, KV head): kRingSplits x 4 heads x (256 o + 2) floats,
+  // addressed from their own base so every buffer offset stays small.
+  const long long group = (long long)(b * kHkv + kvh) * kRingSplits * kGroup;
+  const __amdgpu_buffer_rsrc_t o_rs =
+      __builtin_amdgcn_make_buffer_rsrc(ws_o + group * kD, (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ml_rs =
+      __builtin_amdgcn_make_buffer_rsrc(ws_ml + group * 2, (short)0, 0x7fffffff, 0x00020000);
+  const int o_off = ((sp * kGroup + hl) * kD + d0) * 4;   // bytes
+  const int ml_off = (sp * kGroup + hl) * 8;
   // This workgroup's partial: its waves merged under their largest reference max.
-  const long long part = ((long long)(b * kHkv + kvh) * kRingSplits + sp) * kGroup + hl;
-  {
+  if (mt) {
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kSplitWaves; ++v) M = fmaxf(M, part_ml[v][hl][0]);
@@ -1028,37 +815,53 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
       a0 += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d0]) * wgt;
       a1 += *reinterpret_cast<const f32x4*>(&part_o[v][hl][d0 + 4]) * wgt;
     }
-    *reinterpret_cast<f32x4*>(ws_o + part * kD + d0) = a0;
-    *reinterpret_cast<f32x4*>(ws_o + part * kD + d0 + 4) = a1;
-    if ((tid & 31) == 0) {
-      ws_ml[2 * part] = M;
-      ws_ml[2 * part + 1] = L;
-    }
+    // Device-scope stores (sc1): written through to the level every XCD's accesses
+    // meet, and acknowledged only once they are there.
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a0), o_rs, o_off, 0, kScDevice);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a1), o_rs, o_off + 16, 0,
+                                           kScDevice);
+    if ((tid & 31) == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(M), __float_as_uint(L)}, ml_rs,
+                                            ml_off, 0, kScDevice);
   }
-  // Publish the partial (device-scope release), then count this workgroup in; the last one
-  // of the (KV head, sequence) merges.
-  __threadfence();
+  // Every thread's partial stores are complete before the workgroup counts itself in, so
+  // the last to arrive finds all of them at the device level; no L2 write-back or
+  // invalidate is needed (a device-scope __threadfence would write back and invalidate
+  // the whole L2 of this XCD, once per workgroup).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   unsigned* counter = counters + b * kHkv + kvh;
-  if (tid == 0) last = atomicAdd(counter, 1u) == kRingSplits - 1;
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           kRingSplits - 1;
   __syncthreads();
-  if (!last) return;
-  __threadfence();  // acquire: every other workgroup's partial is visible
+  if (!last || !mt) return;
 
-  const long long part0 = ((long long)(b * kHkv + kvh) * kRingSplits) * kGroup + hl;
+  // Device-scope loads (sc1) of the other workgroups' partials: never served from a line
+  // cached before they were written.
+  float mv[kRingSplits], lv[kRingSplits];
+#pragma unroll
+  for (int s = 0; s < kRingSplits; ++s) {
+    const u32x2 ml =
+        __builtin_amdgcn_raw_buffer_load_b64(ml_rs, (s * kGroup + hl) * 8, 0, kScDevice);
+    mv[s] = __uint_as_float(ml[0]);
+    lv[s] = __uint_as_float(ml[1]);
+  }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kRingSplits; ++s) M = fmaxf(M, ws_ml[2 * (part0 + s * kGroup)]);
+  for (int s = 0; s < kRingSplits; ++s) M = fmaxf(M, mv[s]);
   const float M_use = M == -INFINITY ? 0.f : M;
   float L = 0.f;
   f32x4 a0 = f32x4{}, a1 = f32x4{};
 #pragma unroll
   for (int s = 0; s < kRingSplits; ++s) {
-    const long long ps = part0 + s * kGroup;
-    const float wgt = fast_exp2(ws_ml[2 * ps] - M_use);
-    L += ws_ml[2 * ps + 1] * wgt;
-    a0 += *reinterpret_cast<const f32x4*>(ws_o + ps * kD + d0) * wgt;
-    a1 += *reinterpret_cast<const f32x4*>(ws_o + ps * kD + d0 + 4) * wgt;
+    const int off = ((s * kGroup + hl) * kD + d0) * 4;
+    const f32x4 o0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(o_rs, off, 0, kScDevice));
+    const f32x4 o1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(o_rs, off + 16, 0, kScDevice));
+    const float wgt = fast_exp2(mv[s] - M_use);
+    L += lv[s] * wgt;
+    a0 += o0 * wgt;
+    a1 += o1 * wgt;
   }
   const float sg = 1.f / (1.f + expf(-gate_logit));
   const float f = L > 0.f ? sg / L : 0.f;
@@ -1066,7 +869,8 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
       uint4{pack_bf16x2(a0[0] * f, a0[1] * f), pack_bf16x2(a0[2] * f, a0[3] * f),
             pack_bf16x2(a1[0] * f, a1[1] * f), pack_bf16x2(a1[2] * f, a1[3] * f)};
   if ((tid & 31) == 0 && lse != nullptr) lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  if (tid == 0) *counter = 0u;  // ready for the next step (kernel boundaries order it)
+  if (tid == 0)  // ready for the next step (kernel boundaries order it)
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Clears n 32-bit counters (a kernel, not a memset, so that it can sit in a captured graph).
@@ -1141,15 +945,47 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
 }
 
 size_t ring_step_workspace_bytes(int B) {
-  if (B > kRingSplitMaxB) return 0;  // the fused kernel needs none
-  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
+  const size_t parts = (size_t)B * kHkv * ring_splits(B) * kGroup;
   return parts * (kD + 2) * sizeof(float) + (size_t)B * kHkv * sizeof(unsigned);
 }
 
+namespace {
+
+// The ring kernel's partials and counters in a workspace of ring_step_workspace_bytes(B).
+struct RingWs {
+  float* o;
+  float* ml;
+  unsigned* counters;
+};
+RingWs ring_ws(void* workspace, int B) {
+  const size_t parts = (size_t)B * kHkv * ring_splits(B) * kGroup;
+  float* o = static_cast<float*>(workspace);
+  return RingWs{o, o + parts * kD, reinterpret_cast<unsigned*>(o + parts * (kD + 2))};
+}
+
+template <bool kAppend>
+hipError_t launch_ring_split(const bf16_t* q, const bf16_t* k_new, const bf16_t* v_new,
+                             bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,
+                             const bf16_t* gate, bf16_t* out, float* lse, const RopeTable& tab,
+                             float scale_log2e, void* workspace, int rope_q, hipStream_t stream) {
+  const RingWs ws = ring_ws(workspace, B);
+  // splits x waves = 16: one 32-key step per wave over the 512 slots.
+  if (ring_splits(B) == 8) {
+    hipLaunchKernelGGL((ring_split_kernel<kAppend, 8, 2>), dim3(kHkv * 8, (unsigned)B),
+                       dim3(64 * 2), 0, stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out,
+                       lse, tab, scale_log2e, ws.o, ws.ml, ws.counters, rope_q);
+  } else {
+    hipLaunchKernelGGL((ring_split_kernel<kAppend, 4, 4>), dim3(kHkv * 4, (unsigned)B),
+                       dim3(64 * 4), 0, stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out,
+                       lse, tab, scale_log2e, ws.o, ws.ml, ws.counters, rope_q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t clear_ring_counters(void* workspace, int B, hipStream_t stream) {
-  if (B > kRingSplitMaxB) return hipSuccess;
-  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
-  unsigned* counters = reinterpret_cast<unsigned*>(static_cast<float*>(workspace) + parts * (kD + 2));
+  unsigned* counters = ring_ws(workspace, B).counters;
   const int n = B * kHkv;
   hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      counters, n);
@@ -1160,51 +996,20 @@ hipError_t launch_ring_step(const bf16_t* q, const bf16_t* k_new, const bf16_t* 
                             bf16_t* k_ring, bf16_t* v_ring, const int* pos, int B,
                             const bf16_t* gate, bf16_t* out, float* lse, const RopeTable& tab,
                             float scale_log2e, void* workspace, hipStream_t stream) {
-  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = ws_o + parts * kD;
-  unsigned* counters = reinterpret_cast<unsigned*>(ws_ml + parts * 2);
-  // Split for B <= 2 only: each split workgroup's device-scope fence (an L2 write-back and
-  // invalidate) grows with the workgroup count.  Measured per step through the driver:
-  // B = 1 10.4 us split against 16.8 fused, B = 2 13.4 against 17.0, B = 4 19.6 against 17.2.
-  if (B <= kRingSplitMaxB) {
-    hipLaunchKernelGGL(ring_split_kernel<true>, dim3(kHkv * kRingSplits, (unsigned)B),
-                       dim3(64 * kSplitWaves), 0, stream, q, k_new, v_new, k_ring, v_ring, pos,
-                       gate, out, lse, tab, scale_log2e, ws_o, ws_ml, counters, 1);
-  } else {
-    hipLaunchKernelGGL(ring_step_kernel<true>, dim3(kHkv, (unsigned)B), dim3(64 * kRingWaves),
-                       0, stream, q, k_new, v_new, k_ring, v_ring, pos, gate, out, lse, tab,
-                       scale_log2e, 1);
-  }
-  return hipGetLastError();
+  return launch_ring_split<true>(q, k_new, v_new, k_ring, v_ring, pos, B, gate, out, lse, tab,
+                                 scale_log2e, workspace, 1, stream);
 }
 
 hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_t* v_ring,
                               const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
                               bool rope_q, const RopeTable& tab, float scale_log2e,
                               void* workspace, hipStream_t stream) {
-  if (B > kRingSplitMaxB) {
-    // Query heads split over kGroup / kHeadsNH workgroups per (KV head, b); no workspace.
-    constexpr int kSplit = kGroup / kHeadsNH;
-    const unsigned grid = 8u * kSplit * (unsigned)((B * kHkv + 7) / 8);
-    hipLaunchKernelGGL((ring_heads_kernel<kHeadsNH, kHeadsWaves>), dim3(grid),
-                       dim3(64 * kHeadsWaves), 0, stream, q, k_ring, v_ring, pos, B, gate, out,
-                       lse, tab, scale_log2e, rope_q ? 1 : 0);
-    return hipGetLastError();
-  }
   const hipError_t e = clear_ring_counters(workspace, B, stream);
   if (e != hipSuccess) return e;
-  const size_t parts = (size_t)B * kHkv * kRingSplits * kGroup;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = ws_o + parts * kD;
-  unsigned* counters = reinterpret_cast<unsigned*>(ws_ml + parts * 2);
   // The ring is only read (k_new / v_new unused without the append).
-  hipLaunchKernelGGL(ring_split_kernel<false>, dim3(kHkv * kRingSplits, (unsigned)B),
-                     dim3(64 * kSplitWaves), 0, stream, q, nullptr, nullptr,
-                     const_cast<bf16_t*>(k_ring), const_cast<bf16_t*>(v_ring), pos, gate, out,
-                     lse, tab, scale_log2e, ws_o, ws_ml, counters, rope_q ? 1 : 0);
-  return hipGetLastError();
+  return launch_ring_split<false>(q, nullptr, nullptr, const_cast<bf16_t*>(k_ring),
+                                  const_cast<bf16_t*>(v_ring), pos, B, gate, out, lse, tab,
+                                  scale_log2e, workspace, rope_q ? 1 : 0, stream);
 }
-
 
 }  // namespace hattn

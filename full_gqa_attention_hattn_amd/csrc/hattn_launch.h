@@ -65,17 +65,15 @@ hipError_t launch_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v
 // One decode step of a sliding layer in one launch: rotate K by pos and append K / V at
 // ring slot pos mod 512 of k_ring / v_ring [B, 512, 4, 256], then attend (Q-RoPE fused),
 // gate and store out [B, 1, 16, 256] (and lse [B, 1, 16] unless null).  q, k_new, v_new
-// are the token's un-rotated projections [B, 1, *, 256].  For B <= 2 the ring is split
-// over 8 workgroups per (sequence, KV head), and workspace (16-byte aligned, at least
-// ring_step_workspace_bytes(B) bytes) holds their partials and one counter per (sequence,
-// KV head), which must be zero before the first step (clear_ring_counters) and which every
-// step leaves at zero; larger batches use one workgroup each and no workspace.
+// are the token's un-rotated projections [B, 1, *, 256].  The ring is split over 8
+// workgroups per (sequence, KV head) for B <= 8, 4 above, and workspace (16-byte aligned,
+// at least ring_step_workspace_bytes(B) bytes) holds their partials and one counter per
+// (sequence, KV head), which must be zero before the first step (clear_ring_counters) and
+// which every step leaves at zero.
 size_t ring_step_workspace_bytes(int B);
 // The ring attention of a plain sliding decode (the token's key and value already in the
-// ring; q rotated unless rope_q), for every B >= 1: at B <= 2 it clears the split kernel's
-// counters and launches it, in that order, on `stream`; above, it launches the head-split
-// kernel (kGroup / 2 workgroups per (sequence, KV head), no merge between them) and uses
-// no workspace.
+// ring; q rotated unless rope_q), for every B >= 1: it clears the split kernel's counters
+// and launches it, in that order, on `stream`.
 hipError_t launch_ring_decode(const bf16_t* q, const bf16_t* k_ring, const bf16_t* v_ring,
                               const int* pos, int B, const bf16_t* gate, bf16_t* out, float* lse,
                               bool rope_q, const RopeTable& tab, float scale_log2e,

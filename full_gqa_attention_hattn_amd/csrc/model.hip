@@ -91,14 +91,17 @@ hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, 
   if (pos == nullptr) return HATTN_ERR_NULL;
   st = check_layers(layers, n_layers);
   if (st != HATTN_OK) return st;
-  if (workspace == nullptr || workspace_bytes < hattn_model_decode_workspace_bytes(n_layers, B, cap))
-    return HATTN_ERR_WORKSPACE;
+  const size_t need = hattn_model_decode_workspace_bytes(n_layers, B, cap);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
   if (!a16(workspace) || (reinterpret_cast<uintptr_t>(pos) & 3u)) return HATTN_ERR_ALIGN;
   hattn_layer_cfg sliding;
   hattn_cfg_preset(HATTN_SLIDING, &sliding);
   const hattn::RopeTable sliding_tab = hattn::rope_table(&sliding);
   const float sliding_scale = hattn::scale_log2e(&sliding);
-  void* ring_ws = static_cast<char*>(workspace) + full_region_bytes(n_layers, B, cap);
+  // Null when nothing needs a workspace (sliding layers only, at batches whose ring kernels
+  // keep no partials).
+  void* ring_ws = workspace == nullptr ? nullptr
+                                       : static_cast<char*>(workspace) + full_region_bytes(n_layers, B, cap);
   {
     const hipError_t e = hattn::clear_ring_counters(ring_ws, B, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hattn::note_hip_error(e);
@@ -108,7 +111,7 @@ hattn_status hattn_model_decode(const hattn_layer_io* layers, int32_t n_layers, 
     hattn_layer_cfg cfg;
     hattn_cfg_preset(kind_of(l), &cfg);
     if (cfg.kind == HATTN_SLIDING) {
-      // Append, ring attention and merge in one launch (the 512-slot ring needs no split).
+      // Append, ring attention and merge in one launch.
       const hipError_t e = hattn::launch_ring_step(
           static_cast<const hattn::bf16_t*>(L.q), static_cast<const hattn::bf16_t*>(L.k),
           static_cast<const hattn::bf16_t*>(L.v), static_cast<hattn::bf16_t*>(L.k_cache),

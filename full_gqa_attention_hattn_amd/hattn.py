@@ -363,7 +363,7 @@ def _layer_array(where, layers, cap, pos_name, pos, workspace):
         a(pre + "v_cache", L.get("v_cache"), _BF16, (B, rows, 4, 256))
         _attn_out_args(a, B, S, L.get("gate"), L.get("out"), L.get("lse"), prefix=pre)
     a(pos_name, pos, _I32, numel=B)
-    a("workspace", workspace, _U8)
+    a("workspace", workspace, _U8, optional=True)   # the library says when one is needed
     a.done()
     arr = (LayerIO * len(layers))()
     for i, L in enumerate(layers):
@@ -384,16 +384,18 @@ def model_prefill_workspace_bytes(n_layers: int, B: int, Sq: int) -> int:
 def model_decode(layers, cap: int, pos, workspace, stream=None):
     """One decode step of every layer; layers: list of dicts with the LayerIO fields."""
     arr, B, _ = _layer_array("model_decode", layers, cap, "pos", pos, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.hattn_model_decode(arr, len(layers), cap, _ptr(pos), B, _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+                                   ws_bytes, _stream(stream)),
            "hattn_model_decode")
 
 
 def model_prefill(layers, cap: int, pos0, workspace, stream=None):
     """One prefill chunk through every layer (chunks in position order)."""
     arr, B, Sq = _layer_array("model_prefill", layers, cap, "pos0", pos0, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.hattn_model_prefill(arr, len(layers), cap, _ptr(pos0), B, Sq, _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(),
+                                    ws_bytes,
                                     _stream(stream)), "hattn_model_prefill")
 
 

@@ -167,8 +167,7 @@ hattn_status hattn_prefill_ring(const hattn_layer_cfg* cfg, const void* q, const
 
 /* Bytes of device workspace hattn_decode needs for B sequences and this cache capacity:
  * a full layer's split-KV partial results; a sliding layer's ring-split partials and
- * arrival counters at B <= 2, and 0 above (no workspace).  0 also for an invalid
- * configuration. */
+ * arrival counters.  0 for an invalid configuration. */
 size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32_t cap);
 
 /* Single-token decode.  q [B,1,16,256] (rotated unless flags & HATTN_ROPE_Q_FUSED),
@@ -180,14 +179,13 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
  *            order from position 0), and every valid slot is visible.
  * Same arithmetic as hattn_prefill.  The key range is split into chunks whose partial
  * (max, sum, output) triples are merged by log-sum-exp in a second kernel.  A sliding
- * layer runs as one kernel instead.  At B <= 2, 8 workgroups per (sequence, KV head) each
- * take 64 ring slots, and the last of them to finish merges the 8 partials; its arrival
- * counters live in the workspace and the call clears them first, so calls that share a
- * workspace must be ordered (one stream); they race otherwise.  Above B = 2 the 4 query
- * heads of each (sequence, KV head) are split over 2 workgroups, each covering the whole
- * ring for its 2 heads and merging its waves' partials itself; no workspace is used.
+ * layer runs as one kernel instead: 8 workgroups per (sequence, KV head) for B <= 8, 4
+ * above, each take an equal share of the 512 ring slots, and the last of them to finish
+ * merges their partials; the arrival counters live in the workspace and the call clears
+ * them first (a small kernel ahead of it on `stream`), so calls that share a workspace
+ * must be ordered (one stream); they race otherwise.
  * workspace: device, at least hattn_decode_workspace_bytes(cfg, B, cap) bytes (16-byte
- * aligned); may be NULL when that size is 0.
+ * aligned).
  * B <= 65535 (one grid row per sequence), else HATTN_ERR_SHAPE.
  * [T2] "The real bottleneck of a million-token context" (the ring keeps the last 512
  * tokens); [T1] "GQA, fused projection and output gating". */
@@ -288,7 +286,7 @@ typedef struct hattn_layer_io {
 } hattn_layer_io;
 
 /* Device workspace hattn_model_decode needs (0 for invalid sizes): the full layers' split
- * partials and, for B <= 2, the sliding layers' ring partials and per-head counters.  Its
+ * partials and the sliding layers' ring partials and per-head counters.  Its
  * contents between calls do not matter: each call clears the counters (with a kernel) before
  * its first sliding layer. */
 size_t hattn_model_decode_workspace_bytes(int32_t n_layers, int32_t B, int32_t cap);

@@ -166,10 +166,11 @@ def test_decode_validation_and_workspace(h):
     f, s = _cfg(h, "full"), _cfg(h, "sliding")
     need = lib.hattn_decode_workspace_bytes(f, 32, 131136)
     assert need > 0 and need % 16 == 0
-    # sliding layers: the ring split's partials and counters at B <= 2, nothing above
-    assert lib.hattn_decode_workspace_bytes(s, 2, 512) > 0
-    assert lib.hattn_decode_workspace_bytes(s, 3, 512) == 0
-    assert lib.hattn_decode_workspace_bytes(s, 32, 512) == 0
+    # sliding layers: the ring split's partials (8 splits up to B = 8, 4 above; 4 heads x
+    # (256 + 2) floats each) and a counter per (sequence, KV head)
+    for B, splits in ((1, 8), (2, 8), (8, 8), (9, 4), (32, 4)):
+        assert lib.hattn_decode_workspace_bytes(s, B, 512) == \
+            B * 4 * splits * 4 * 258 * 4 + B * 4 * 4, B
     assert lib.hattn_decode_workspace_bytes(s, 32, 513) == 0
     assert lib.hattn_decode_workspace_bytes(f, -1, 8) == 0
 
@@ -191,8 +192,8 @@ def test_decode_validation_and_workspace(h):
 
 
 def test_decode_fp8_workspace_holds_the_split_for_both_kinds(h):
-    """The 8-bit decode splits the keys for both layer kinds, so its workspace is the split
-    partials even where the bf16 sliding decode needs none (B > 2)."""
+    """The 8-bit decode splits the keys for both layer kinds (a sliding layer's window of
+    the position-indexed cache too), so its workspace is the split-KV partials."""
     lib = h.lib()
     f, s = _cfg(h, "full"), _cfg(h, "sliding")
     for B in (1, 2, 3, 32):

@@ -236,8 +236,7 @@ def _decode_case(h, kind, positions, cap, seed, fused):
         h.rope_qk(cfg, q, None, pos)
     out = torch.empty_like(q)
     lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
-    # sliding layers above two sequences need no workspace: pass none
-    ws = h.alloc_workspace(cfg, B, cap) if kind == "full" or B <= 2 else None
+    ws = h.alloc_workspace(cfg, B, cap)
     h.decode(cfg, q, K, V, pos, new["gate"], out, lse, ws, rope_q_fused=fused)
     torch.cuda.synchronize()
     # a decode only reads the caches (the ring kernels take them through const_cast)
@@ -255,9 +254,10 @@ def test_decode_full_cache(h, fused):
 
 
 @pytest.mark.parametrize("positions", [
-    [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9, (1 << 31) - 1],  # B > 2 ring kernel
-    [131072],                                # B = 1 and 2: the ring split in one launch
+    [0, 5, 510, 511, 512, 131072, (1 << 20), (1 << 30) + 9, (1 << 31) - 1],  # 4 splits above B = 8
+    [131072],                                # 8 splits up to B = 8
     [300, (1 << 31) - 1],
+    [0, 33, 300, (1 << 31) - 1],             # 8 splits, partly filled rings
 ])
 @pytest.mark.parametrize("fused", [True, False])
 def test_decode_ring(h, fused, positions):
@@ -267,16 +267,17 @@ def test_decode_ring(h, fused, positions):
 
 
 def test_decode_ring_workspace_reuse(h):
-    """The one-kernel sliding decode (B <= 2) keeps arrival counters in the caller's
-    workspace.  Each call clears them itself, so a workspace full of 0xFF bytes works, and
-    calls that share one workspace (B = 2, then 1, then 2 again) each match the oracle; the
-    repeated call gives the same bits."""
+    """The one-kernel sliding decode keeps arrival counters in the caller's workspace.
+    Each call clears them itself, so a workspace full of 0xFF bytes works, and calls that
+    share one workspace (B = 2, 1, 12 with its other split count and counter offset, then
+    2 again) each match the oracle; the repeated call gives the same bits."""
     say("decode ring workspace reuse")
     cfg = h.preset("sliding")
-    ws = h.alloc_workspace(cfg, 2, 512)
+    ws = h.alloc_workspace(cfg, 12, 512)
     ws.fill_(0xFF)
     outs = []
-    for positions, seed in (([700, 131072], 83), ([5000], 85), ([700, 131072], 83)):
+    twelve = [700 + 1000 * i for i in range(11)] + [131072]
+    for positions, seed in (([700, 131072], 83), ([5000], 85), (twelve, 87), ([700, 131072], 83)):
         B = len(positions)
         new = synth.layer_inputs(seed, B, 1, "cuda")
         cache = synth.cache_inputs(seed + 1, B, 512, 512, "cuda")
@@ -291,7 +292,7 @@ def test_decode_ring_workspace_reuse(h):
                             _cpu(new["gate"][b, 0]), p, "sliding")
             check_outputs(out[b, 0], lse[b, 0], y, l, f"reuse B={B} p={p}")
         outs.append((out.clone(), lse.clone()))
-    assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+    assert torch.equal(outs[0][0], outs[3][0]) and torch.equal(outs[0][1], outs[3][1])
 
 
 def test_decode_equals_prefill_row(h):

@@ -118,11 +118,12 @@ def test_model_prefill_chunks_then_decode(h):
             check_outputs(outs[l][b], lses[l][b], y, lse, f"model layer {l} ({kind}) b={b}")
 
 
-@pytest.mark.parametrize("positions", [[1000], [5, 1000, 2000]])
+@pytest.mark.parametrize("positions", [[1000], [5, 1000, 2000],
+                                       [5, 100, 511, 512, 1000, 1500, 2000, 2047, 7, 700]])
 def test_model_decode_graph_replay(h, positions):
     """A captured decode step of a 4-layer schedule replays to the eager result, several
-    times, with other work and synchronisations in between.  B = 1 takes the split ring
-    step (its counters cleared by a kernel in the graph), B = 3 the fused one."""
+    times, with other work and synchronisations in between.  The ring steps' counters are
+    cleared by a kernel in the graph; B = 1 and 3 split each ring 8 ways, B = 10 4 ways."""
     say(f"model decode graph replay B={len(positions)}")
     n_layers, B, cap = 4, len(positions), 2048
     layers = _model_layers(h, n_layers, B, 1, cap, 161)
@@ -175,17 +176,27 @@ def test_model_decode_graph_replay(h, positions):
             check_outputs(ref[l][0][b, 0], ref[l][1][b, 0], y, lse, f"graph layer {l} b={b}")
 
 
-def test_model_decode_sliding_at_far_positions(h):
-    """Three sliding layers (the fused ring step) at positions far past the model's context,
-    up to the largest int32 position: the rotated key lands in slot p mod 512 and the
-    token attends the whole ring, as the oracle's decode over the same ring."""
-    say("model decode far positions")
-    n_layers, B = 3, 2
-    positions = [(1 << 30) + 5, (1 << 31) - 1]
+@pytest.mark.parametrize("positions", [
+    [(1 << 30) + 5, (1 << 31) - 1],                       # far past the context, to int32 max
+    [0, 1, 31, 32, 63, 300, 511],                         # 8 splits, rings partly filled
+    [0, 1, 31, 32, 63, 64, 300, 511, 512, 131072, (1 << 30) + 5, (1 << 31) - 1],  # 4 splits
+])
+def test_model_decode_sliding_steps(h, positions):
+    """Three sliding layers (the fused ring step: append, attention, merge) at positions
+    from 0 up to the largest int32 position: the rotated key lands in slot p mod 512, the
+    token attends the ring's filled slots (unfilled ones hold NaN here and must not reach
+    the output), as the oracle's decode over the same ring."""
+    B = len(positions)
+    say(f"model decode sliding steps B={B}")
+    n_layers = 3
     layers = _model_layers(h, n_layers, B, 1, 512, 171)
     before = []
     for l, L in enumerate(layers):
         ring = synth.cache_inputs(172 + l, B, 512, 512, "cuda")
+        for b, p in enumerate(positions):
+            if p < 511:     # slots p + 1 .. 511 have never been written
+                ring["cache_k"][b, p + 1:] = NAN
+                ring["cache_v"][b, p + 1:] = NAN
         L["k_cache"].copy_(ring["cache_k"])
         L["v_cache"].copy_(ring["cache_v"])
         before.append((_cpu(L["k_cache"]).clone(), _cpu(L["v_cache"]).clone()))
@@ -193,6 +204,7 @@ def test_model_decode_sliding_at_far_positions(h):
                      device="cuda")
     h.model_decode(layers, 512, synth.positions(positions, B, "cuda"), ws)
     torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16)     # NaN-safe equality of bf16 rows
     for l, L in enumerate(layers):
         for b, p in enumerate(positions):
             _, kr = O.rope_qk(None, _cpu(L["k"][b]), p, "sliding")
@@ -200,10 +212,11 @@ def test_model_decode_sliding_at_far_positions(h):
             K[p % 512] = kr[0].to(torch.bfloat16)
             V[p % 512] = _cpu(L["v"][b, 0])
             got_k = _cpu(L["k_cache"][b])
-            assert torch.equal(got_k[torch.arange(512) != p % 512], K[torch.arange(512) != p % 512])
+            other = torch.arange(512) != p % 512
+            assert torch.equal(bits(got_k[other]), bits(K[other]))
+            assert torch.equal(bits(_cpu(L["v_cache"][b])), bits(V))
             assert_bf16_close(got_k[p % 512], kr[0], f"ring key layer {l} p={p}")
-            assert torch.equal(_cpu(L["v_cache"][b]), V)
             assert_rotated(got_k[p % 512], kr[0], got_k[p % 512], 256, f"ring key layer {l} p={p}")
             # the oracle attends over its own ring: the snapshot with its own rotated key
             y, lse = O.decode(_cpu(L["q"][b, 0]), K, V, _cpu(L["gate"][b, 0]), p, "sliding")
-            check_outputs(L["out"][b, 0], L["lse"][b, 0], y, lse, f"model far layer {l} p={p}")
+            check_outputs(L["out"][b, 0], L["lse"][b, 0], y, lse, f"model step layer {l} p={p}")

@@ -25,13 +25,14 @@ def _cpu(t):
     return t.detach().cpu()
 
 
-# (kind, positions, cap): per kind, a larger call then a smaller one.  Sliding: B = 3
-# (the head-split ring kernel, no scratch) after B = 2 and 1 (the ring split, whose
-# partials and arrival counters live in the scratch).
+# (kind, positions, cap): per kind, a larger call then a smaller one.  Sliding: B = 2 and
+# 1 (8 ring splits), then B = 12 (4 splits); the partials and arrival counters live in
+# the scratch.
 CASES = {
     "full": [([131072, 70000, 5, 131071, 100000, 2, 90000, 131000], 131136),
              ([4000, 777], 4096)],
-    "sliding": [([131072, 600], 512), ([300], 512), ([5000, 1 << 20, 40], 512)],
+    "sliding": [([131072, 600], 512), ([300], 512),
+                ([5000, 1 << 20, 40, 0, 511, 512, 131072, 77, 300, 9999, (1 << 31) - 1, 1000], 512)],
 }
 
 
