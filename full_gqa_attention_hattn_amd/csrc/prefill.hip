@@ -173,7 +173,10 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   constexpr int kTile = kBN * kD * 2;        // bytes of one K or V tile
   constexpr int kPitch = kHalf + 2;          // cos/sin table row, f32x2; +16 B vs bank aliasing
   constexpr int kCsBytes = kBQ * kPitch * 8;
-  constexpr int kRingBytes = 5 * kTile;     // K tiles: 2 stages, V tiles: 3 stages
+  // 32-key tiles per barrier: 2 on full layers (their one workgroup per CU can take all
+  // 160 KiB of LDS), 1 on sliding layers (two workgroups per CU share it).
+  constexpr int kTPI = kSliding ? 1 : 2;
+  constexpr int kRingBytes = 5 * kTPI * kTile;  // K tiles: 2 stages, V tiles: 3, of kTPI each
   constexpr int kLdsBytes = kRingBytes > kCsBytes ? kRingBytes : kCsBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
@@ -324,13 +327,16 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
   // the same scheme on full layers was 0.7% slower than the static one).
   if (rb == 0) __builtin_amdgcn_s_setprio(2);
 
-  // K tiles rotate through two LDS stages and V tiles through three.  Iteration t first
-  // runs the PV step of tile t - 1 (its probabilities wait in registers), then issues the
-  // copies of tile t + 1, then QK and the softmax of tile t.  So the transposing V reads
-  // follow a barrier that has already drained the copies, and the issue of the next
-  // copies overlaps the PV MFMAs still in the pipe.
+  // K tiles rotate through two LDS stages and V tiles through three, each stage holding
+  // kTPI tiles.  An iteration takes the kTPI tiles from t: it first runs the PV steps of
+  // the previous iteration's tiles (their probabilities wait in registers), then issues
+  // the copies of the next kTPI tiles, then QK and the softmax of its own.  So the
+  // transposing V reads follow a barrier that has already drained the copies, and the
+  // issue of the next copies overlaps the PV MFMAs still in the pipe.  With two tiles per
+  // barrier the softmax of the last wave to finish its QK, which nothing else on its SIMD
+  // overlaps before the barrier, comes once per 64 keys instead of once per 32.
   char* const kring = smem;
-  char* const vring = smem + 2 * kTile;
+  char* const vring = smem + 2 * kTPI * kTile;
   auto qk_softmax = [&](const char* kst, int t, bf16x8* pfo) __attribute__((always_inline)) {
     // S^T[key][query]; accumulator element 4i + j of lane half hh is key 8i + 4hh + j.
     // K fragments are read two ahead of the MFMA that consumes them.
@@ -443,25 +449,59 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 1);
   };
 
-  if (t_lo <= t_hi) load_tile(kring, vring, t_lo);
-  bf16x8 pf[2];
-  bool have_p = false;
-  int vcur = 0;  // V stage of tile t
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const int it = t - t_lo;
-    // Tile t has landed for every wave, and every wave is done with iteration t - 1.
-    wait_lds_dma<0>();
-    __syncthreads();
-    const int vprev = vcur == 0 ? 2 : vcur - 1;
-    const int vnext = vcur == 2 ? 0 : vcur + 1;
-    if (kSliding) __builtin_amdgcn_s_setprio(2);
-    if (have_p) pv(vring + vprev * kTile, pf);
-    if (t + 1 <= t_hi) load_tile(kring + ((it + 1) & 1) * kTile, vring + vnext * kTile, t + 1);
-    have_p = t >= wt_lo && t <= wt_hi;
-    if (have_p) qk_softmax(kring + (it & 1) * kTile, t, pf);
-    vcur = vnext;
+  if constexpr (kTPI == 1) {
+    if (t_lo <= t_hi) load_tile(kring, vring, t_lo);
+    bf16x8 pf[2];
+    bool have_p = false;
+    int vcur = 0;  // V stage of tile t
+    for (int t = t_lo; t <= t_hi; ++t) {
+      const int it = t - t_lo;
+      // Tile t has landed for every wave, and every wave is done with iteration t - 1.
+      wait_lds_dma<0>();
+      __syncthreads();
+      const int vprev = vcur == 0 ? 2 : vcur - 1;
+      const int vnext = vcur == 2 ? 0 : vcur + 1;
+      if (kSliding) __builtin_amdgcn_s_setprio(2);
+      if (have_p) pv(vring + vprev * kTile, pf);
+      if (t + 1 <= t_hi) load_tile(kring + ((it + 1) & 1) * kTile, vring + vnext * kTile, t + 1);
+      have_p = t >= wt_lo && t <= wt_hi;
+      if (have_p) qk_softmax(kring + (it & 1) * kTile, t, pf);
+      vcur = vnext;
+    }
+    if (have_p) pv(vring + (vcur == 0 ? 2 : vcur - 1) * kTile, pf);
+  } else {
+    // Two tiles per barrier: PV of the previous iteration's second tile, the copies of the
+    // next two, then QK, softmax and PV of tile t, then QK and softmax of tile t + 1, whose
+    // probabilities wait for the next iteration.  Only one tile's probabilities are live
+    // across the barrier.
+    if (t_lo <= t_hi) load_tile(kring, vring, t_lo);
+    if (t_lo + 1 <= t_hi) load_tile(kring + kTile, vring + kTile, t_lo + 1);
+    bf16x8 pf[2];
+    bool have_p = false;
+    int vcur = 0;  // V stage of tiles t, t + 1
+    for (int t = t_lo; t <= t_hi; t += 2) {
+      const int kcur = ((t - t_lo) >> 1) & 1;  // their K stage
+      // Tiles t and t + 1 have landed for every wave, and every wave is done with the
+      // previous iteration.
+      wait_lds_dma<0>();
+      __syncthreads();
+      const int vprev = vcur == 0 ? 2 : vcur - 1;
+      const int vnext = vcur == 2 ? 0 : vcur + 1;
+      if (have_p) pv(vring + (2 * vprev + 1) * kTile, pf);
+      if (t + 2 <= t_hi)
+        load_tile(kring + (2 * (kcur ^ 1)) * kTile, vring + (2 * vnext) * kTile, t + 2);
+      if (t + 3 <= t_hi)
+        load_tile(kring + (2 * (kcur ^ 1) + 1) * kTile, vring + (2 * vnext + 1) * kTile, t + 3);
+      if (t >= wt_lo && t <= wt_hi) {
+        qk_softmax(kring + (2 * kcur) * kTile, t, pf);
+        pv(vring + (2 * vcur) * kTile, pf);
+      }
+      have_p = t + 1 <= t_hi && t + 1 >= wt_lo && t + 1 <= wt_hi;
+      if (have_p) qk_softmax(kring + (2 * kcur + 1) * kTile, t + 1, pf);
+      vcur = vnext;
+    }
+    if (have_p) pv(vring + (2 * (vcur == 0 ? 2 : vcur - 1) + 1) * kTile, pf);
   }
-  if (have_p) pv(vring + (vcur == 0 ? 2 : vcur - 1) * kTile, pf);
 
   float l_a, l_b;
   halves(l_run, &l_a, &l_b);
