@@ -319,13 +319,13 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       ld.load_split(vd, vrbase, vbase, key0, pb, kmax - pb, w);
     }
   };
-  // The two waves sharing a SIMD (row blocks 0 and 1 of one head) would otherwise reach
-  // their softmax phases together; issue priority for row block 0 staggers them.  Sliding
-  // workgroups have one row block, and the waves sharing a SIMD belong to two workgroups:
-  // there each wave raises its priority while it issues the PV MFMAs, the copies and the
-  // QK chain, and drops it for the softmax (measured 0.6-0.8% on the 32K sliding prefill;
-  // the same scheme on full layers was 0.7% slower than the static one).
-  if (rb == 0) __builtin_amdgcn_s_setprio(2);
+  // Sliding workgroups have one row block, and the waves sharing a SIMD belong to two
+  // workgroups: there each wave raises its priority while it issues the PV MFMAs, the copies
+  // and the QK chain, and drops it for the softmax (measured 0.6-0.8% on the 32K sliding
+  // prefill).  Full layers run at one priority: with two tiles per barrier, a raised
+  // priority for row block 0 (which staggered the softmax phases of the two waves sharing a
+  // SIMD at one tile per barrier) measured 0.3-0.6% slower.
+  if (kSliding) __builtin_amdgcn_s_setprio(2);
 
   // K tiles rotate through two LDS stages and V tiles through three, each stage holding
   // kTPI tiles.  An iteration takes the kTPI tiles from t: it first runs the PV steps of
