@@ -35,6 +35,28 @@ def test_exports_every_declared_symbol(h):
         assert hasattr(lib, name), name
 
 
+def test_header_serves_a_plain_c_caller(tmp_path):
+    """include/hattn.h compiles as strict C99 and C++17, and a C program linked against
+    libhattn.so gets the documented presets, sizes, schedule, validation codes and status
+    strings (tests/c_abi_smoke.c; nothing there touches a GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        subprocess.run([gcc if lang == "c" else (shutil.which("g++") or gcc), std, "-Wall",
+                        "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", lang,
+                        str(HEADER)], check=True)
+    exe = tmp_path / "c_abi_smoke"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", str(HEADER.parent), str(ROOT / "tests" / "c_abi_smoke.c"),
+                    "-L", str(LIBPATH.parent), "-lhattn", f"-Wl,-rpath,{LIBPATH.parent}",
+                    "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
 def test_presets(h):
     s, f = h.preset("sliding"), h.preset("full")
     assert (s.kind, s.window, s.rot_dim, s.rope_theta) == (0, 512, 256, 1e4)
