@@ -176,7 +176,9 @@ size_t hattn_decode_workspace_bytes(const hattn_layer_cfg* cfg, int32_t B, int32
  *   full:    k_cache / v_cache [B,cap,4,256], keys at rows 0 .. pos[b] (clipped to cap);
  *   sliding: the ring [B,window,4,256] (cap must equal window); the first
  *            min(pos[b] + 1, window) slots are valid (the ring is filled in position
- *            order from position 0), and every valid slot is visible.
+ *            order from position 0), and every valid slot is visible.  All 512 slots
+ *            are read (their loads go out before the position is known); the others
+ *            may hold anything, NaN included, and never reach the result.
  * Same arithmetic as hattn_prefill.  The key range is split into chunks whose partial
  * (max, sum, output) triples are merged by log-sum-exp in a second kernel.  A sliding
  * layer runs as one kernel instead: 8 workgroups per (sequence, KV head) for B <= 8, 4
