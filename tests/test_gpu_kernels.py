@@ -266,6 +266,19 @@ def test_decode_ring(h, fused, positions):
     _decode_case(h, "sliding", positions, 512, 81, fused)
 
 
+def test_decode_ring_many_sequences(h):
+    """B = 100: the ring kernel's 1600 workgroups (4 per (sequence, KV head)) take more than
+    one round of the CUs, so arrivals on one counter come from workgroups that were never
+    resident together; every sequence matches the oracle."""
+    import random
+    rng = random.Random(97)
+    positions = [rng.choice([rng.randrange(0, 512), rng.randrange(512, 1 << 20),
+                             rng.randrange(1 << 20, (1 << 31) - 1)]) for _ in range(100)]
+    positions[:3] = [0, 511, (1 << 31) - 1]
+    say(f"decode ring B={len(positions)}")
+    _decode_case(h, "sliding", positions, 512, 91, True)
+
+
 def test_decode_ring_workspace_reuse(h):
     """The one-kernel sliding decode keeps arrival counters in the caller's workspace.
     Each call clears them itself, so a workspace full of 0xFF bytes works, and calls that

@@ -180,6 +180,7 @@ def test_model_decode_graph_replay(h, positions):
     [(1 << 30) + 5, (1 << 31) - 1],                       # far past the context, to int32 max
     [0, 1, 31, 32, 63, 300, 511],                         # 8 splits, rings partly filled
     [0, 1, 31, 32, 63, 64, 300, 511, 512, 131072, (1 << 30) + 5, (1 << 31) - 1],  # 4 splits
+    [(37 * b * b + 11 * b) % 1500 for b in range(40)],   # 640 workgroups: several rounds
 ])
 def test_model_decode_sliding_steps(h, positions):
     """Three sliding layers (the fused ring step: append, attention, merge) at positions
