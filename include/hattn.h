@@ -206,7 +206,8 @@ hattn_status hattn_decode(const hattn_layer_cfg* cfg, const void* q, const void*
  * looks up that device's copy of the array (the calling thread's current device, which
  * must be the device of `stream` and of the buffers) and keeps its address.
  *   HATTN_ERR_SCRATCH: hattn_decode_workspace_bytes(cfg, B, cap) exceeds
- *     HATTN_DECODE_NOALLOC_MAX_BYTES (a full layer at B up to about 2000 fits); nothing is
+ *     HATTN_DECODE_NOALLOC_MAX_BYTES (a full layer at B up to about 2000 fits, a sliding
+ *     layer at B up to 507); nothing is
  *     enqueued.  Other errors as hattn_decode.
  * Every call on one GPU shares that GPU's array and leaves its contents behind; each call
  * clears what must start at zero.  Calls that overlap on one GPU (on different streams, or

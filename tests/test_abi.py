@@ -418,3 +418,9 @@ def test_decode_noalloc_validation(h):
     # the largest measured shapes fit
     assert lib.hattn_decode_workspace_bytes(f, 32, 131136) <= h.DECODE_NOALLOC_MAX_BYTES
     assert lib.hattn_decode_workspace_bytes(f, 1, (1 << 20) + 64) <= h.DECODE_NOALLOC_MAX_BYTES
+    # sliding layers: 4 ring splits of 4 x 258 floats per (sequence, KV head) and a counter,
+    # 66112 bytes a sequence, so 507 sequences fit in 32 MiB and 508 do not
+    per_seq = 4 * 4 * 4 * 258 * 4 + 4 * 4
+    assert lib.hattn_decode_workspace_bytes(s, 507, 512) == 507 * per_seq <= h.DECODE_NOALLOC_MAX_BYTES
+    assert lib.hattn_decode_workspace_bytes(s, 508, 512) > h.DECODE_NOALLOC_MAX_BYTES
+    assert call(cfg=s, cap=512, B=508) == h.HATTN_ERR_SCRATCH
