@@ -210,23 +210,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   if (rope_q && qlane) {
     // Rotate-half pairs (d, d + r/2) both live in this lane: fragment dc pairs with dc + kNdc.
 #pragma unroll
-    for (int dc = 0; dc < kNdc; ++dc) {
-      const bf16x8 xa = qf[dc], xb = qf[dc + kNdc];
-      f32x4 ya0, ya1, yb0, yb1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
+    for (int dc = 0; dc < kNdc; ++dc)
+      rope_fragments(qf[dc], qf[dc + kNdc], [&](int e) {
         float sv, cv;
         sincos_angle(rope_angle(p, tab.inv_freq[32 * dc + 8 * g + e]), &sv, &cv);
-        const float a = (float)xa[e], bb = (float)xb[e];
-        float ya, yb;
-        rope_pair(a, bb, cv, sv, &ya, &yb);
-        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
-      }
-      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
-      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
-      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      qf[dc + kNdc] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    }
+        return f32x2{cv, sv};
+      });
   }
 
   const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
@@ -313,22 +302,12 @@ void decode_split_fp8_kernel(
   }
   if (rope_q && qlane) {
 #pragma unroll
-    for (int dc = 0; dc < kNdc; ++dc) {
-      const bf16x8 xa = qf[dc], xb = qf[dc + kNdc];
-      f32x4 ya0, ya1, yb0, yb1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
+    for (int dc = 0; dc < kNdc; ++dc)
+      rope_fragments(qf[dc], qf[dc + kNdc], [&](int e) {
         float sv, cv;
         sincos_angle(rope_angle(p, tab.inv_freq[32 * dc + 8 * g + e]), &sv, &cv);
-        float ya, yb;
-        rope_pair((float)xa[e], (float)xb[e], cv, sv, &ya, &yb);
-        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
-      }
-      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
-      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
-      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      qf[dc + kNdc] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    }
+        return f32x2{cv, sv};
+      });
   }
 
   constexpr long long rs = kHkv * kD;  // bytes per cache row (4 heads x 256 codes)
@@ -716,21 +695,8 @@ __global__ __launch_bounds__(64 * kSplitWaves) void ring_split_kernel(
   // Q^T rotated with the shared table (every lane, so that the repeats stay head 0's).
   if (rope_q) {
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-      const bf16x8 xa = qf[dc], xb = qf[dc + 4];
-      f32x4 ya0, ya1, yb0, yb1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f32x2 c = cs[32 * dc + 8 * g + e];
-        float ya, yb;
-        rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
-        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
-      }
-      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
-      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
-      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      qf[dc + 4] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-    }
+    for (int dc = 0; dc < 4; ++dc)
+      rope_fragments(qf[dc], qf[dc + 4], [&](int e) { return cs[32 * dc + 8 * g + e]; });
   }
 
   // Slots [k_begin, k_end) of this wave: the ring's first min(p + 1, 512) slots are filled

@@ -117,6 +117,25 @@ __device__ __forceinline__ void rope_pair(float a, float b, float c, float s, fl
   *yb = __builtin_fmaf(b, c, __fmul_rn(a, s));
 }
 
+// Rotates the rotate-half pairs held by one lane in two 8-element Q fragments: xa holds
+// dims d .. d + 7 and xb their partners d + r/2 .. d + r/2 + 7; cs(e) returns the (cos, sin)
+// of element e's angle.  The results are rounded to bf16 in place.
+template <class CosSin>
+__device__ __forceinline__ void rope_fragments(bf16x8& xa, bf16x8& xb, CosSin cs) {
+  f32x4 ya0, ya1, yb0, yb1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const f32x2 c = cs(e);
+    float ya, yb;
+    rope_pair((float)xa[e], (float)xb[e], c.x, c.y, &ya, &yb);
+    if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
+  }
+  const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
+  const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
+  xa = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  xb = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 }  // namespace hattn

@@ -265,20 +265,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
 #pragma unroll
     for (int dc = 0; dc < kNdc; ++dc) {
       const f32x2* c8 = cs + (r0 + n) * kPitch + 16 * dc + 8 * hh;
-      const bf16x8 xa = qf[dc], xb = qf[dc + kNdc];
-      f32x4 ya0, ya1, yb0, yb1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f32x2 c = c8[e];
-        const float a = (float)xa[e], bb = (float)xb[e];
-        float ya, yb;
-        rope_pair(a, bb, c.x, c.y, &ya, &yb);
-        if (e < 4) { ya0[e] = ya; yb0[e] = yb; } else { ya1[e - 4] = ya; yb1[e - 4] = yb; }
-      }
-      const bf16x4 a0 = __builtin_convertvector(ya0, bf16x4), a1 = __builtin_convertvector(ya1, bf16x4);
-      const bf16x4 b0 = __builtin_convertvector(yb0, bf16x4), b1 = __builtin_convertvector(yb1, bf16x4);
-      qf[dc] = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      qf[dc + kNdc] = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      rope_fragments(qf[dc], qf[dc + kNdc], [&](int e) { return c8[e]; });
     }
     __syncthreads();  // the cos/sin table shares LDS with the first tiles
   }
