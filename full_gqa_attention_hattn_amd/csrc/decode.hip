@@ -34,6 +34,13 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kRescaleLog2 = 8.f;  // move the reference max only when beaten by 2^8
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Lane src's value of an 8-element bf16 fragment (four 32-bit lane shuffles).
+__device__ __forceinline__ bf16x8 shfl_bf16x8(bf16x8 x, int src) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  return __builtin_bit_cast(bf16x8, uint4{(unsigned)__shfl((int)u.x, src), (unsigned)__shfl((int)u.y, src),
+                                          (unsigned)__shfl((int)u.z, src), (unsigned)__shfl((int)u.w, src)});
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -310,6 +317,24 @@ void decode_split_fp8_kernel(
       });
   }
 
+  // K loads take 16 contiguous codes a lane: MFMA dc covers, in lane group g, dims
+  // 64 (dc >> 1) + 16 g + 8 (dc & 1) .. + 7, so MFMAs 2m and 2m + 1 read one 16-byte piece.
+  // Q^T moves to the same mapping once (it was loaded and rotated as dims 32 dc + 8 g, where
+  // each rotary pair sits in one lane): new (g, dc) is old fragment 2 (dc >> 1) + (g >> 1)
+  // of lane group 2 (g & 1) + (dc & 1), same column.
+  {
+    bf16x8 qn[8];
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) {
+      const int src = n16 + 16 * (2 * (g & 1) + (dc & 1));
+      const bf16x8 v0 = shfl_bf16x8(qf[2 * (dc >> 1)], src);
+      const bf16x8 v1 = shfl_bf16x8(qf[2 * (dc >> 1) + 1], src);
+      qn[dc] = (g >> 1) ? v1 : v0;
+    }
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) qf[dc] = qn[dc];
+  }
+
   constexpr long long rs = kHkv * kD;  // bytes per cache row (4 heads x 256 codes)
   const long long kv_off = ((long long)b * cap * kHkv + kvh) * kD;
   const uint8_t* kb = kc + kv_off;
@@ -327,25 +352,42 @@ void decode_split_fp8_kernel(
   // scores, zero probabilities), so the loads are unconditional and the compiler can count
   // them; each array is refilled for the next step as soon as this step has consumed it
   // (the last step reloads its final row), keeping loads in flight during the arithmetic.
-  uint2 kraw[2][8];
-  float kscale[2][4], vscale[2][4];
+  uint4 kraw[2][4];
+  f32x4 kscale[2], vscale[2];
+  // Scales of keys k0 + 16 blk + 4 g .. + 3 (consecutive in the [B, 4, cap] arrays) as one
+  // 16-byte buffer load when cap keeps them 16-byte aligned; the buffer's range ends at the
+  // row's cap keys (reads past it return zero).  Keys past k_end are masked below.
+  const bool vec_scales = (cap & 3) == 0;
+  const __amdgpu_buffer_rsrc_t ks_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ks), (short)0, cap * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vs_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(vs), (short)0, cap * 4, 0x00020000);
   uint4 vraw[8];
   auto load_k = [&](int k0) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int key = min(k0 + 16 * blk + n16, k_end - 1);
-      const uint8_t* kr = kb + (long long)key * rs + 8 * g;
+      const uint8_t* kr = kb + (long long)key * rs + 16 * g;
 #pragma unroll
-      for (int dc = 0; dc < 8; ++dc) kraw[blk][dc] = *reinterpret_cast<const uint2*>(kr + 32 * dc);
+      for (int m = 0; m < 4; ++m) kraw[blk][m] = *reinterpret_cast<const uint4*>(kr + 64 * m);
     }
+    if (vec_scales) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = min(k0 + 16 * blk + 4 * g + j, k_end - 1);
-        kscale[blk][j] = ks[key];
-        vscale[blk][j] = vs[key];
+      for (int blk = 0; blk < 2; ++blk) {
+        const int off = 4 * (k0 + 16 * blk + 4 * g);
+        kscale[blk] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ks_rs, off, 0, 0));
+        vscale[blk] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vs_rs, off, 0, 0));
       }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = min(k0 + 16 * blk + 4 * g + j, k_end - 1);
+          kscale[blk][j] = ks[key];
+          vscale[blk][j] = vs[key];
+        }
+    }
   };
   auto load_v = [&](int k0) {
 #pragma unroll
@@ -365,11 +407,12 @@ void decode_split_fp8_kernel(
     for (int dc = 0; dc < 8; ++dc) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const uint2 w = kraw[blk][dc];
-        const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
-        const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
-        const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
-        const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+        const uint4 w4 = kraw[blk][dc >> 1];
+        const uint32_t wx = (dc & 1) ? w4.z : w4.x, wy = (dc & 1) ? w4.w : w4.y;
+        const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, 1.0f, false);
+        const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, 1.0f, true);
+        const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, 1.0f, false);
+        const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, 1.0f, true);
         const bf16x8 kf = bf16x8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
         sacc[blk] = mfma16(kf, qf[dc], sacc[blk]);
       }
@@ -383,7 +426,8 @@ void decode_split_fp8_kernel(
         const int key = k0 + 16 * blk + 4 * g + j;
         const float v = key < k_end ? sacc[blk][j] * kscale[blk][j] * sl2 : -INFINITY;
         sv[blk][j] = v;
-        vsc[blk][j] = vscale[blk][j];
+        // masked keys may read scales of rows never written: zero, so no NaN meets P = 0
+        vsc[blk][j] = key < k_end ? vscale[blk][j] : 0.f;
         mloc = fmaxf(mloc, v);
       }
     load_k(kn);

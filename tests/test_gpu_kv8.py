@@ -129,6 +129,40 @@ def test_decode_fp8_matches_oracle(h, kind, fused):
         check_outputs(out[b, 0], lse[b, 0], y, l, f"decode_fp8 {kind} p={p} fused={fused}")
 
 
+@pytest.mark.parametrize("cap", [3000, 3001])
+def test_decode_fp8_unwritten_rows_and_odd_cap(h, cap):
+    """Rows past each sequence's position hold NaN codes (0x7F) and NaN scales, as a cache
+    whose tail was never written may: they must not reach the output.  cap 3000 takes the
+    16-byte scale loads, cap 3001 (rows not 16-byte aligned) the per-key ones."""
+    say(f"decode_fp8 unwritten rows cap={cap}")
+    cfg = h.preset("full")
+    positions = [0, 31, 1000, cap - 2]
+    B = len(positions)
+    new = synth.layer_inputs(177, B, 1, "cuda")
+    cache = synth.cache_inputs(178, B, cap, cap, "cpu")
+    Kc = torch.empty(B, cap, 4, 256, dtype=torch.uint8)
+    Vc = torch.empty_like(Kc)
+    Ks = torch.empty(B, 4, cap)
+    Vs = torch.empty_like(Ks)
+    for b, p in enumerate(positions):
+        Kc[b], Vc[b], Ks[b], Vs[b] = _oracle_cache8(cache["cache_k"][b], cache["cache_v"][b])
+        Kc[b, p + 1:] = 0x7F
+        Vc[b, p + 1:] = 0x7F
+        Ks[b, :, p + 1:] = float("nan")
+        Vs[b, :, p + 1:] = float("nan")
+    Kd, Vd, Ksd, Vsd = Kc.cuda(), Vc.cuda(), Ks.cuda(), Vs.cuda()
+    out = torch.empty_like(new["q"])
+    lse = torch.empty(B, 1, 16, dtype=torch.float32, device="cuda")
+    ws = h.alloc_workspace_fp8(cfg, B, cap)
+    h.decode_fp8(cfg, new["q"], Kd, Vd, Ksd, Vsd, synth.positions(positions, B, "cuda"),
+                 new["gate"], out, lse, ws, rope_q_fused=True)
+    torch.cuda.synchronize()
+    for b, p in enumerate(positions):
+        y, l = O.decode_kv8(_cpu(new["q"][b, 0]), Kc[b], Vc[b], Ks[b].T, Vs[b].T,
+                            _cpu(new["gate"][b, 0]), p, "full")
+        check_outputs(out[b, 0], lse[b, 0], y, l, f"decode_fp8 unwritten cap={cap} p={p}")
+
+
 def test_decode_fp8_follows_append_fp8(h):
     """End to end: append a sequence with the rotating 8-bit append, decode its last token;
     the result matches the oracle's decode over the oracle-quantized rotated keys."""
