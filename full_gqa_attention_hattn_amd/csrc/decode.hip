@@ -18,6 +18,9 @@
 // rescaled.  It writes a partial (reference max, sum, o[4][256]) per (b, kv head, chunk).
 // Phase 2 (decode_combine_kernel): per (b, query head, 32-dim slice), merges the chunk
 // partials by log-sum-exp, applies 1/l and the sigmoid gate, stores bf16 (and the LSE).
+// Sliding layers instead run ring_split_kernel: one launch whose workgroups split each
+// ring and whose last arriver merges their partials (with the append fused in for the
+// schedule driver).  The 8-bit cache runs decode_split_fp8_kernel with the same combine.
 #include "hattn_device.h"
 #include "hattn_launch.h"
 
