@@ -360,11 +360,13 @@ void decode_split_fp8_kernel(
   // Scales of keys k0 + 16 blk + 4 g .. + 3 (consecutive in the [B, 4, cap] arrays) as one
   // 16-byte buffer load when cap keeps them 16-byte aligned; the buffer's range ends at the
   // row's cap keys (reads past it return zero).  Keys past k_end are masked below.
-  const bool vec_scales = (cap & 3) == 0;
+  // (Byte offsets and the range are 32-bit: capacities from 2^29 keys take the per-key path.)
+  const bool vec_scales = (cap & 3) == 0 && cap < (1 << 29);
+  const int scale_bytes = vec_scales ? cap * 4 : 0;
   const __amdgpu_buffer_rsrc_t ks_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ks), (short)0, cap * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ks), (short)0, scale_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vs_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(vs), (short)0, cap * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(vs), (short)0, scale_bytes, 0x00020000);
   uint4 vraw[8];
   auto load_k = [&](int k0) {
 #pragma unroll
