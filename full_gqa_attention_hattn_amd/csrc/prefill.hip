@@ -306,12 +306,12 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       ld.load_split(vd, vrbase, vbase, key0, pb, kmax - pb, w);
     }
   };
-  // Sliding workgroups have one row block, and the waves sharing a SIMD belong to two
-  // workgroups: there each wave raises its priority while it issues the PV MFMAs, the copies
-  // and the QK chain, and drops it for the softmax (measured 0.6-0.8% on the 32K sliding
-  // prefill).  Full layers run at one priority: with two tiles per barrier, a raised
-  // priority for row block 0 (which staggered the softmax phases of the two waves sharing a
-  // SIMD at one tile per barrier) measured 0.3-0.6% slower.
+  // Each wave raises its issue priority while it issues the PV MFMAs, the copies and the QK
+  // chain, and drops it for the softmax, so that the other wave on its SIMD (on sliding
+  // layers, of another workgroup) keeps the MFMA pipe busy meanwhile: 0.6-0.8% on the 32K
+  // sliding prefill, 0.4% on the full 1M chunk.  (A static raised priority for row block 0
+  // of the full layers, which staggered the softmax phases at one tile per barrier, was
+  // 0.3-0.6% slower with two tiles per barrier.)
   if (kSliding) __builtin_amdgcn_s_setprio(2);
 
   // K tiles rotate through two LDS stages and V tiles through three, each stage holding
@@ -348,7 +348,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    if (kSliding) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
 
     const int key0 = t * kBN;
     const bool whole = (key0 <= Pw0 - (kBN - 1)) && (key0 <= capk - kBN) &&  // no key0 + kBN:
@@ -474,6 +474,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       __syncthreads();
       const int vprev = vcur == 0 ? 2 : vcur - 1;
       const int vnext = vcur == 2 ? 0 : vcur + 1;
+      __builtin_amdgcn_s_setprio(2);
       if (have_p) pv(vring + (2 * vprev + 1) * kTile, pf);
       if (t + 2 <= t_hi)
         load_tile(kring + (2 * (kcur ^ 1)) * kTile, vring + (2 * vnext) * kTile, t + 2);
@@ -481,6 +482,7 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
         load_tile(kring + (2 * (kcur ^ 1) + 1) * kTile, vring + (2 * vnext + 1) * kTile, t + 3);
       if (t >= wt_lo && t <= wt_hi) {
         qk_softmax(kring + (2 * kcur) * kTile, t, pf);
+        __builtin_amdgcn_s_setprio(2);
         pv(vring + (2 * vcur) * kTile, pf);
       }
       have_p = t + 1 <= t_hi && t + 1 >= wt_lo && t + 1 <= wt_hi;
