@@ -461,6 +461,13 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
     // next two, then QK, softmax and PV of tile t, then QK and softmax of tile t + 1, whose
     // probabilities wait for the next iteration.  Only one tile's probabilities are live
     // across the barrier.
+    //
+    // Row block 0 runs that last PV before the barrier instead.  The two waves sharing a
+    // SIMD are w and w + 4, one of each row block.  With the same order in both, the row
+    // block 0 wave ran ahead and waited about 900 clocks per iteration at the barrier while
+    // its partner finished QK and softmax alone, so the MFMA pipe idled during that softmax.
+    // Moving one PV step across the barrier for one of the two offsets them, and each
+    // softmax then meets the other wave's MFMAs: 2.6% on the 1M chunk, 3.1% at 128K.
     if (t_lo <= t_hi) load_tile(kring, vring, t_lo);
     if (t_lo + 1 <= t_hi) load_tile(kring + kTile, vring + kTile, t_lo + 1);
     bf16x8 pf[2];
@@ -487,6 +494,13 @@ void prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
       }
       have_p = t + 1 <= t_hi && t + 1 >= wt_lo && t + 1 <= wt_hi;
       if (have_p) qk_softmax(kring + (2 * kcur + 1) * kTile, t + 1, pf);
+      if (rb == 0) {
+        if (have_p) {
+          __builtin_amdgcn_s_setprio(2);
+          pv(vring + (2 * vcur + 1) * kTile, pf);
+        }
+        have_p = false;
+      }
       vcur = vnext;
     }
     if (have_p) pv(vring + (2 * (vcur == 0 ? 2 : vcur - 1) + 1) * kTile, pf);
